@@ -1,0 +1,30 @@
+"""Seeded synthetic inputs shared by the oracle-side tests and the GPU path.
+
+This package builds inputs only: post-RoPE keys with planted near-duplicate
+clusters, value vectors, per-head capacities and random retained sets.  It
+holds none of the scoring, selection or repair arithmetic; both the oracle
+and the HIP library consume what it produces.
+"""
+from .configs import CONFIGS, Config, get_config
+from .generator import (
+    bf16_bits_to_f32,
+    dirichlet_capacities,
+    f64_to_bf16_bits,
+    gumbel_retained,
+    make_head,
+    make_heads,
+    rope_tables,
+)
+
+__all__ = [
+    "CONFIGS",
+    "Config",
+    "get_config",
+    "bf16_bits_to_f32",
+    "f64_to_bf16_bits",
+    "dirichlet_capacities",
+    "gumbel_retained",
+    "make_head",
+    "make_heads",
+    "rope_tables",
+]

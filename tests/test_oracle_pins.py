@@ -1,0 +1,437 @@
+"""Pins for the fp64 oracle: worked examples printed on the pages, closed forms,
+invariants, exhaustive search and brute force on tiny inputs.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped +1, >=
+for >, a window off by one, a missing normalisation, a wrong tie order, a swap
+ranked the wrong way) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import brute
+from oracle import twinkv_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# score: the Figure 3 example and the reversal condition
+
+
+def test_figure3_normalised_scores():
+    g = _golden("figure3_example.json")
+    N = g["N"]
+    e = np.array([g["A"]["energy"], g["B"]["energy"]])
+    c = np.array([2, 0])  # A carries a count-2 key, B a count-0 key
+    s, w = O.frequency_score(e, c, N)
+    tol = 0.5 * 10 ** -g["printed_decimals"]
+    assert abs(e[0] * w[0] - g["A"]["normalized_score"]) <= tol
+    assert abs(e[1] * w[1] - g["B"]["normalized_score"]) <= tol
+    # the rank reversal: A has more energy, B ranks higher after weighting
+    assert e[0] > e[1] and s[1] > s[0]
+    # the other assignment of the printed counts cannot reproduce the numbers
+    s2, w2 = O.frequency_score(e, np.array([0, 2]), N)
+    assert abs(e[0] * w2[0] - g["A"]["normalized_score"]) > tol
+
+
+def test_discount_closed_forms():
+    N = 1000
+    c = np.arange(N)
+    s, w = O.frequency_score(np.ones(N), c, N)
+    assert w[0] == 1.0  # a key with no twin keeps its full energy
+    assert s[0] == pytest.approx(math.log(N + 1))
+    assert np.all(np.diff(s) < 0)  # more twins, smaller score
+    assert np.all(w > 0) and np.all(w <= 1)
+    # c = N would make the discount log(1) = 0; one below keeps it positive
+    assert s[-1] == pytest.approx(math.log((N + 1) / N))
+    # energy scales the score linearly
+    s3, _ = O.frequency_score(np.full(N, 3.0), c, N)
+    np.testing.assert_allclose(s3, 3 * s, rtol=0, atol=0)
+
+
+def test_reversal_condition():
+    """For e_i > e_j > 0, weighting reverses their order iff
+    1 < e_i/e_j < d_j/d_i (section 3.2 of the frequency-correction page)."""
+    rng = np.random.default_rng(5)
+    N = 4096
+    for _ in range(2000):
+        ei, ej = sorted(rng.uniform(0.1, 2.0, 2), reverse=True)
+        if ei == ej:
+            continue
+        ci, cj = rng.integers(0, 20, 2)
+        s, _ = O.frequency_score(np.array([ei, ej]), np.array([ci, cj]), N)
+        di, dj = math.log((N + 1) / (ci + 1)), math.log((N + 1) / (cj + 1))
+        assert (s[0] < s[1]) == (1 < ei / ej < dj / di)
+
+
+# ---------------------------------------------------------------------------
+# budget and protection: the printed boundary examples
+
+
+def test_short_prefix_clipping_example():
+    g = _golden("short_prefix_example.json")
+    B = O.uniform_budget(g["N"], g["removal"])
+    assert B == g["budget"]
+    s, r = O.protected_counts(B, g["sink_param"], g["recent_param"])
+    assert (s, r, B - s - r) == (g["sinks"], g["recent"], g["unprotected"])
+    rng = np.random.default_rng(0)
+    keep, idx = O.select_head(rng.random(g["N"]), rng.random(g["N"]), B, g["sink_param"], g["recent_param"])
+    expect = list(range(4)) + list(range(g["N"] - 39, g["N"]))
+    assert idx.tolist() == expect
+
+
+def test_two_head_budget_example():
+    g = _golden("budget_conservation.json")
+    B = O.uniform_budget(g["N"], g["removal"])
+    s, r = O.protected_counts(B, 4, 64)
+    assert (B, s + r, B - s - r) == (g["B"], g["P"], g["U"])
+    assert sum(g["capacities"]) == 2 * B
+    assert min(g["capacities"]) >= g["P"] + g["U"] // 2 == g["min_capacity"]
+    rng = np.random.default_rng(1)
+    for cap in g["capacities"]:
+        keep, idx = O.select_head(rng.random(g["N"]), rng.random(g["N"]), cap, 4, 64)
+        assert keep.sum() == cap and idx.size == cap
+
+
+def test_budget_floor():
+    assert O.uniform_budget(10, 0.35) == 6  # 6.5 -> 6: floor, not ceil or round
+    assert O.uniform_budget(8192, 0.7) == 2457
+    assert O.uniform_budget(32768, 0.5) == 16384
+    assert O.uniform_budget(131072, 0.75) == 32768
+    assert O.uniform_budget(7, 0.0) == 7
+
+
+def test_protection_clipping_small_capacities():
+    assert O.protected_counts(0, 4, 64) == (0, 0)
+    assert O.protected_counts(3, 4, 64) == (3, 0)  # sinks take priority
+    assert O.protected_counts(10, 4, 64) == (4, 6)
+    assert O.protected_counts(100, 4, 64) == (4, 64)
+
+
+# ---------------------------------------------------------------------------
+# similarity, count and best twin: closed forms
+
+
+def _rows(N, idx_vec):
+    return np.array(idx_vec, dtype=np.float64)
+
+
+def test_strict_threshold_at_exact_cosine():
+    # (1,0) and (3,4): cosine exactly 3/5
+    d, N, w = 4, 8, 2
+    K = np.zeros((N, d))
+    K[:, 2] = 1.0  # filler orthogonal to both
+    K[0] = [1, 0, 0, 0]
+    K[5] = [3, 4, 0, 0]
+    c, b, a = O.twin_count_and_best(K, 0.6, w)
+    assert b[0] == 0.6 and a[0] == 5 and c[0] == 0 and c[5] == 0  # sim == tau is not a twin
+    c, _, _ = O.twin_count_and_best(K, 0.5999, w)
+    assert c[0] == 1 and c[5] == 1
+
+
+def test_window_boundary():
+    d, N, w = 4, 12, 3
+    K = np.zeros((N, d))
+    K[:, 3] = 1.0
+    K[2] = [1, 1, 0, 0]
+    K[2 + w] = [2, 2, 0, 0]  # |i-j| = w: local, excluded
+    K[2 + w + 1] = [0.5, 0.5, 0, 0]  # |i-j| = w+1: counted
+    c, b, a = O.twin_count_and_best(K, 0.9, w)
+    assert c[2] == 1 and a[2] == 2 + w + 1 and b[2] == 1.0
+    assert c[2 + w] == 0  # its only copies are within the window
+    assert c[2 + w + 1] == 1 and a[2 + w + 1] == 2
+
+
+def test_orthogonal_keys_zero_count():
+    d = 32
+    N = d
+    K = np.diag(np.arange(1, N + 1, dtype=np.float64))  # orthogonal, different norms
+    w = 4
+    c, b, a = O.twin_count_and_best(K, 0.5, w)
+    assert np.all(c == 0)
+    assert np.all(b == 0.0)
+    for i in range(N):
+        assert a[i] == (0 if i > w else i + w + 1)  # lowest eligible position
+
+
+def test_planted_exact_duplicates_scale_invariant():
+    rng = np.random.default_rng(2)
+    d, N, w = 16, 64, 4
+    K = rng.integers(-8, 9, size=(N, d)).astype(np.float64)
+    base = K[10].copy()
+    for p, scale in [(20, 2.0), (40, 0.5), (12, 4.0), (63, 1.0)]:
+        K[p] = scale * base  # exact multiples: cosine exactly 1
+    c, b, a = O.twin_count_and_best(K, 0.99, w)
+    # 10's nonlocal copies: 20, 40, 63 (12 is inside the window)
+    assert c[10] == 3 and b[10] == 1.0 and a[10] == 20
+    assert c[12] == 3 and a[12] == 20  # 12 sees 20, 40, 63 (10 is local)
+    assert c[20] == 4 and a[20] == 10
+
+
+def test_no_eligible_positions():
+    rng = np.random.default_rng(3)
+    for N, w in [(1, 0), (5, 4), (33, 32), (2, 1)]:
+        K = rng.standard_normal((N, 8))
+        c, b, a = O.twin_count_and_best(K, 0.1, w)
+        assert np.all(c == 0) and np.all(b == -1.0) and np.all(a == -1)
+
+
+def test_antiparallel_and_zero_keys():
+    d, N, w = 4, 6, 1
+    K = np.zeros((N, d))
+    K[0] = [1, 2, 0, 0]
+    K[3] = [-1, -2, 0, 0]
+    # positions 1, 2, 4, 5 are zero keys: similarity 0 with everything
+    c, b, a = O.twin_count_and_best(K, 0.5, w)
+    assert c[0] == 0
+    assert b[0] == 0.0 and a[0] == 2  # zero keys (sim 0) beat the antiparallel one (-1)
+    K2 = np.zeros((3, d))
+    K2[0] = [1, 2, 0, 0]
+    K2[2] = [-1, -2, 0, 0]
+    c, b, a = O.twin_count_and_best(K2, 0.5, 1)
+    assert b[0] == -1.0 and a[0] == 2  # a real maximum of -1, told apart by a >= 0
+    assert b[1] == -1.0 and a[1] == -1  # nothing eligible
+
+
+def test_count_invariants_random():
+    rng = np.random.default_rng(4)
+    d, N, w = 8, 200, 5
+    K = rng.standard_normal((N, d))
+    for _ in range(30):  # plant some near-duplicates
+        i, j = rng.integers(0, N, 2)
+        K[j] = K[i] + 0.01 * rng.standard_normal(d)
+    tau = 0.8
+    c, b, a = O.twin_count_and_best(K, tau, w)
+    n = O.squared_norms(K)
+    S = O.cosine_rows(K, n, np.arange(N))
+    ok = O.nonlocal_mask(np.arange(N), np.arange(N), w)
+    T = (S > tau) & ok
+    assert np.array_equal(T, T.T)  # the twin relation is symmetric
+    assert c.sum() % 2 == 0
+    assert np.array_equal(c, T.sum(1))
+    assert np.all(b[:, None] >= np.where(ok, S, -np.inf))
+    assert np.all((b >= -1) & (b <= 1 + 1e-15))
+    for i in range(N):
+        assert ok[i, a[i]] and S[i, a[i]] == b[i]
+        assert not np.any(S[i, : a[i]][ok[i, : a[i]]] == b[i])  # lowest index on ties
+
+
+def test_oracle_matches_brute_force_tiny():
+    rng = np.random.default_rng(6)
+    for trial in range(6):
+        N, d = int(rng.integers(20, 70)), int(rng.choice([4, 8]))
+        w = int(rng.integers(0, 6))
+        K = np.round(rng.standard_normal((N, d)) * 4) / 4  # coarse grid: many exact ties
+        for _ in range(6):
+            i, j = rng.integers(0, N, 2)
+            K[j] = K[i] * rng.choice([1.0, 2.0, 0.5])
+        tau = float(rng.choice([0.3, 0.6, 0.9]))
+        c, b, a = O.twin_count_and_best(K, tau, w)
+        bf = brute.twin_stats(K.tolist(), tau, w)
+        assert [x[0] for x in bf] == c.tolist()
+        assert [x[2] for x in bf] == a.tolist()
+        np.testing.assert_allclose([x[1] for x in bf], b, rtol=0, atol=1e-15)
+
+
+def test_best_surviving_twin_restricted_columns():
+    rng = np.random.default_rng(7)
+    N, d, w = 60, 8, 3
+    K = np.round(rng.standard_normal((N, d)) * 4) / 4
+    S0 = (rng.random(N) < 0.5).astype(np.uint8)
+    b, a = O.best_surviving_twin(K, S0, w)
+    bf = brute.twin_stats(K.tolist(), 0.5, w, allowed=S0.tolist())
+    assert [x[2] for x in bf] == a.tolist()
+    np.testing.assert_allclose([x[1] for x in bf], b, rtol=0, atol=1e-15)
+    assert np.all(S0[a[a >= 0]] == 1)
+    # empty retained set: every b is -1
+    b0, a0 = O.best_surviving_twin(K, np.zeros(N, np.uint8), w)
+    assert np.all(b0 == -1) and np.all(a0 == -1)
+
+
+# ---------------------------------------------------------------------------
+# the synthetic generator's planted structure predicts the oracle's counts
+
+
+@pytest.mark.parametrize("cfg_id,N", [(2, 3000), (4, 3000), (5, 2500)])
+def test_planted_clusters_predict_counts(cfg_id, N):
+    from synth import get_config, make_head
+
+    cfg = get_config(cfg_id)
+    h = make_head(cfg, 3, N=N)
+    K = O.widen_bf16(h["K"])
+    c, b, _ = O.twin_count_and_best(K, cfg.tau, cfg.window)
+    cl = h["cluster"]
+    pos = np.arange(N)
+    expect = np.zeros(N, dtype=np.int64)
+    for i in np.flatnonzero(cl >= 0):
+        mates = pos[(cl == cl[i]) & (np.abs(pos - i) > cfg.window)]
+        expect[i] = mates.size
+    assert np.array_equal(c, expect)
+    assert np.all(b[expect > 0] > 0.97)
+
+
+# ---------------------------------------------------------------------------
+# selection
+
+
+def test_select_matches_exhaustive_search():
+    rng = np.random.default_rng(8)
+    for trial in range(40):
+        N = int(rng.integers(6, 12))
+        cap = int(rng.integers(0, N + 1))
+        sink, recent = int(rng.integers(0, 3)), int(rng.integers(0, 3))
+        # coarse values so that exact score and energy ties occur
+        s = rng.integers(0, 3, N).astype(float)
+        e = rng.integers(0, 3, N).astype(float)
+        keep, idx = O.select_head(s, e, cap, sink, recent)
+        assert idx.tolist() == brute.select_exhaustive(s.tolist(), e.tolist(), cap, sink, recent)
+
+
+def test_select_tie_rule_explicit():
+    # equal scores: higher energy wins; equal score and energy: lower position wins
+    s = np.array([0, 5, 5, 5, 5, 0.0])
+    e = np.array([0, 1, 2, 2, 1, 0.0])
+    keep, idx = O.select_head(s, e, 4, 1, 1)  # 1 sink + 1 recent + 2 chosen
+    assert idx.tolist() == [0, 2, 3, 5]
+    keep, idx = O.select_head(s, e, 3, 1, 1)
+    assert idx.tolist() == [0, 2, 5]
+    keep, idx = O.select_head(s, e, 5, 1, 1)
+    assert idx.tolist() == [0, 1, 2, 3, 5]
+
+
+def test_select_invariants_random():
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        N = int(rng.integers(50, 400))
+        cap = int(rng.integers(0, N + 1))
+        s, e = rng.random(N), rng.random(N)
+        keep, idx = O.select_head(s, e, cap, 4, 32)
+        prot = O.protected_mask(N, cap, 4, 32)
+        assert keep.sum() == cap and np.all(keep[prot] == 1)
+        assert np.all(np.diff(idx) > 0)
+        kept_u = np.flatnonzero((keep == 1) & ~prot)
+        drop_u = np.flatnonzero((keep == 0) & ~prot)
+        if kept_u.size and drop_u.size:
+            assert s[kept_u].min() >= s[drop_u].max()
+
+
+# ---------------------------------------------------------------------------
+# repair
+
+
+def _hand_keys():
+    u1, u2, u3, u4 = np.eye(4)
+    K = np.array([u4, u1, u2, u1, u3, u2, u1 + u2, u3, u3 + u4, u1, u2 + u3, u4])
+    return K
+
+
+def test_repair_hand_example():
+    """Twelve positions, window 1, tau 0.9, one sink and one recent slot.
+    S0 = {0, 1, 3, 6, 9, 11}.  Derived by hand:
+    b(S0) = [1, 1, 1/sqrt2, 1, 0, 0, 1/sqrt2, 0, 1/sqrt2, 1, 1/2, 1];
+    orphans by (b asc, i asc) = 4, 5, 7, 10, 2, 8;
+    donors by (b desc, j asc) = 1, 3, 9 (6 has b < tau; 0 and 11 are protected);
+    m = 3, pairs (4,1), (5,3), (7,9); S1 = {0, 4, 5, 6, 7, 11}."""
+    K = _hand_keys()
+    S0 = np.zeros(12, np.uint8)
+    S0[[0, 1, 3, 6, 9, 11]] = 1
+    r = O.repair_head(K, S0, 0.9, 1, 1, 1)
+    h = 1 / math.sqrt(2)
+    np.testing.assert_allclose(r["best"], [1, 1, h, 1, 0, 0, h, 0, h, 1, 0.5, 1], rtol=0, atol=1e-15)
+    assert r["arg"].tolist() == [11, 3, 6, 1, 0, 0, 1, 0, 0, 1, 6, 0]
+    assert r["orphans"].tolist() == [4, 5, 7, 10, 2, 8]
+    assert r["donors"].tolist() == [1, 3, 9]
+    assert r["m"] == 3
+    assert r["pairs"].tolist() == [[4, 1], [5, 3], [7, 9]]
+    assert np.flatnonzero(r["keep"]).tolist() == [0, 4, 5, 6, 7, 11]
+    # the one-shot pass is not idempotent: all copies of u1 left together
+    r2 = O.repair_head(K, r["keep"], 0.9, 1, 1, 1)
+    assert r2["m"] > 0 and 1 in r2["orphans"].tolist()
+
+
+def test_repair_donor_at_exact_tau():
+    # b == tau makes a donor (>=) but a pair with sim == tau is not an orphan's twin (<)
+    K = np.zeros((8, 4))
+    K[:, 2] = 1.0
+    K[1] = [1, 0, 0, 0]
+    K[4] = [3, 4, 0, 0]
+    S0 = np.zeros(8, np.uint8)
+    S0[[1, 4]] = 1
+    r = O.repair_head(K, S0, 0.6, 1, 0, 0)
+    assert r["best"][1] == 0.6 and r["best"][4] == 0.6
+    assert r["donors"].tolist() == [1, 4]  # tie in b: lower position first
+    # evicted filler keys: cos with (1,0,0,0) is 0 and with (3,4,0,0) is 0 -> orphans
+    assert r["n_orphans"] == 6 and r["m"] == 2
+
+
+def test_repair_noop_when_redundancy_consistent():
+    rng = np.random.default_rng(10)
+    for _ in range(20):
+        N, d, w = 80, 16, 2
+        K = rng.standard_normal((N, d))
+        K[40:] = K[:40] * 1.0  # every key has an exact twin 40 positions away
+        S0 = np.zeros(N, np.uint8)
+        S0[rng.permutation(40)[:20]] = 1  # keep one copy of 20 pairs, none of the others
+        r = O.repair_head(K, S0, 0.95, w, 0, 0)
+        # every evicted key with a retained twin is covered; evicted keys whose twin was
+        # also evicted are orphans, but no retained key duplicates another: no donors
+        assert r["n_donors"] == 0 and r["m"] == 0
+        assert np.array_equal(r["keep"], S0)
+        # symmetric case: every evicted key has a surviving twin -> no orphans
+        S0b = np.zeros(N, np.uint8)
+        S0b[:40] = 1
+        rb = O.repair_head(K, S0b, 0.95, w, 0, 0)
+        assert rb["n_orphans"] == 0 and np.array_equal(rb["keep"], S0b)
+
+
+def test_repair_budget_and_pairs_random():
+    rng = np.random.default_rng(11)
+    for _ in range(25):
+        N, d = int(rng.integers(30, 120)), 8
+        w = int(rng.integers(0, 4))
+        K = np.round(rng.standard_normal((N, d)) * 2) / 2
+        for _ in range(N // 4):
+            i, j = rng.integers(0, N, 2)
+            K[j] = K[i]
+        S0 = (rng.random(N) < rng.uniform(0.2, 0.8)).astype(np.uint8)
+        sink, recent = int(rng.integers(0, 3)), int(rng.integers(0, 5))
+        r = O.repair_head(K, S0, 0.9, w, sink, recent)
+        assert r["keep"].sum() == S0.sum()
+        prot = O.protected_mask(N, int(S0.sum()), sink, recent)
+        for o, dn in r["pairs"]:
+            assert S0[o] == 0 and r["keep"][o] == 1
+            assert S0[dn] == 1 and r["keep"][dn] == 0 and not prot[dn]
+        bf = brute.repair(K.tolist(), S0.tolist(), 0.9, w, sink, recent)
+        assert bf["orphans"] == r["orphans"].tolist()
+        assert bf["donors"] == r["donors"].tolist()
+        assert bf["pairs"] == [tuple(p) for p in r["pairs"].tolist()]
+
+
+def test_repair_idempotent_when_twins_touch_protected_positions():
+    """If every twin relation joins a protected position to an unprotected one,
+    and S0 keeps the protected positions, a second pass changes nothing."""
+    rng = np.random.default_rng(12)
+    for _ in range(20):
+        N, d, w = 60, 32, 1
+        sink, recent = 3, 3
+        K = rng.standard_normal((N, d))
+        prot_pos = list(range(sink)) + list(range(N - recent, N))
+        free = np.arange(sink, N - recent)
+        twins = rng.choice(free, size=10, replace=False)
+        for t in twins:
+            K[t] = K[rng.choice(prot_pos)] * 2.0
+        S0 = np.zeros(N, np.uint8)
+        S0[prot_pos] = 1
+        S0[rng.choice(free, size=20, replace=False)] = 1
+        r1 = O.repair_head(K, S0, 0.9, w, sink, recent)
+        r2 = O.repair_head(K, r1["keep"], 0.9, w, sink, recent)
+        assert r2["m"] == 0 and np.array_equal(r2["keep"], r1["keep"])
