@@ -1,0 +1,165 @@
+/*
+ * twinkv.h - C ABI of the MI355X (gfx950) key-redundancy scoring library.
+ *
+ * The library computes, independently for every (batch, layer, KV head) --
+ * called a "head" below, G of them, each with N positions and head dim d --
+ * the quantities of TwinKV-style KV-cache compression:
+ *
+ *   twinkv_score   nonlocal near-duplicate counts, best nonlocal twin
+ *                  (similarity and position), value energy and the
+ *                  frequency-discounted score;
+ *   twinkv_select  exact-budget per-head retention with protected sink and
+ *                  recent positions;
+ *   twinkv_repair  the one-shot orphan/donor swap on a given retained set at
+ *                  a fixed budget.
+ *
+ * Sources (page title and section/equation):
+ *   [P1] "TwinKV: A Composable Repair Pass for KV Cache Eviction via Pairwise
+ *        Key Redundancy" (arXiv HTML): section 3.1, section 3.2 (Eq. 1, Eq. 2,
+ *        protected regions), section 3.4 (Eq. 4, orphans, donors, swap).
+ *   [P2] "Small Frequency Corrections Can Change What Survives KV Cache
+ *        Compression" (paperpeel): section 3.1 (budget, protection), section
+ *        3.2 (count, energy, score, ties), section 3.4 (selection order).
+ *
+ * Conventions for every entry point:
+ *   - Array arguments are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them after the call returns.
+ *   - Per-head arrays are dense, row-major, heads outermost: element (g, i)
+ *     of a [G][N] array is at g*N + i; keys/values [G][N][d] put feature t of
+ *     position i of head g at (g*N + i)*d + t.  Keys and values are bfloat16
+ *     (raw 16-bit patterns), finite.  Pointers must be 16-byte aligned.
+ *   - Positions are 0-based; "|i - j| > window" is shift-invariant, so the
+ *     pages' 1-based formulas carry over unchanged.
+ *   - All work is enqueued asynchronously on `stream` (a hipStream_t, may be
+ *     NULL for the null stream); the call returns before the GPU finishes.
+ *     Arguments are checked on the host first: on any error nothing is
+ *     launched and a negative twinkv_status is returned.  Faults inside the
+ *     kernels surface at the caller's next synchronisation.
+ *   - `workspace` is caller-owned device scratch of at least
+ *     twinkv_workspace_bytes(op, params) bytes (256-byte aligned); it may be
+ *     NULL when that size is 0.  Concurrent calls need distinct workspaces.
+ *   - `marks` is optional (NULL to skip): an array of hipEvent_t created by
+ *     the caller.  When given, the library records marks[k] on `stream`
+ *     immediately before launching phase k and marks[P] after the last
+ *     launch, where P is the phase count documented per entry point.  It
+ *     serves only to time the phases.
+ *   - No exception crosses the ABI; there is no global state.
+ */
+#ifndef TWINKV_H
+#define TWINKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum twinkv_status {
+  TWINKV_OK = 0,
+  TWINKV_ERR_ARG = -1,         /* a null pointer, a size out of range, a bad parameter */
+  TWINKV_ERR_UNSUPPORTED = -2, /* head dim other than 64 or 128                        */
+  TWINKV_ERR_WORKSPACE = -3,   /* workspace smaller than twinkv_workspace_bytes()       */
+  TWINKV_ERR_HIP = -4          /* the HIP runtime refused a launch or an event record   */
+} twinkv_status;
+
+/* Problem description shared by all entry points. */
+typedef struct twinkv_params {
+  int64_t G;      /* number of independent heads (batch * layers * KV heads), >= 1          */
+  int64_t N;      /* prefix length of every head, 1 <= N <= 2^30                             */
+  int32_t d;      /* head dim: 64 or 128                                                    */
+  int32_t window; /* local exclusion w >= 0: j is a twin candidate of i only if |i-j| > w
+                     ([P1] section 3.2; the pages' second page calls it l)                   */
+  double tau;     /* similarity threshold, -1 < tau < 1 ([P1] Eq. 2 uses sim > tau)          */
+  int32_t sink;   /* leading protected positions before clipping, >= 0 ([P2] section 3.1)   */
+  int32_t recent; /* trailing protected positions before clipping, >= 0                     */
+} twinkv_params;
+
+enum { TWINKV_OP_SCORE = 0, TWINKV_OP_SELECT = 1, TWINKV_OP_REPAIR = 2 };
+
+/* Phase counts for the `marks` argument. */
+enum { TWINKV_SCORE_PHASES = 2, TWINKV_SELECT_PHASES = 1, TWINKV_REPAIR_PHASES = 4 };
+
+/* Bytes of workspace an operation needs for these parameters; 0 if the
+ * parameters are invalid (see the entry points) or the op needs none. */
+size_t twinkv_workspace_bytes(int op, const twinkv_params* params);
+
+/* Uniform per-head capacity B = floor(N * (1 - removal)) ([P2] section 3.1,
+ * "Equation 1").  Returns -1 if N < 0 or removal is outside [0, 1]. */
+int64_t twinkv_uniform_capacity(int64_t N, double removal);
+
+/* Human-readable text for a twinkv_status value (static storage). */
+const char* twinkv_status_string(int status);
+
+/*
+ * twinkv_score - per position i of every head:
+ *   count[g][i]    = #{ j : |i-j| > window, sim(i,j) > tau }           ([P1] Eq. 2, [P2] 3.2)
+ *   best_sim[g][i] = max over j with |i-j| > window of sim(i,j), or -1 if no such j;
+ *                    computed exactly in fp64 as dot/sqrt(n_i*n_j) for the chosen j
+ *   best_idx[g][i] = the lowest j attaining best_sim, or -1 if no such j
+ *   energy[g][i]   = ||v_i||^2, exact in fp64                            ([P2] 3.2)
+ *   score[g][i]    = energy * ln((N+1)/(count+1)), fp64                  ([P2] 3.2)
+ *   omega[g][i]    = ln((N+1)/(count+1)) / ln(N+1) (optional: may be NULL)
+ * where sim(i,j) = k_i.k_j / (||k_i|| ||k_j||) is the cosine of the
+ * post-RoPE keys ([P1] Eq. 1) and is 0 when either key is zero.
+ * Protected positions take part in the counts ([P2] 3.2).
+ * keys, values: bf16 [G][N][d].  count, best_idx: int32 [G][N].
+ * best_sim, energy, score, omega: double [G][N].
+ * Phases for `marks`: 0 = norms and energies, 1 = fused Gram, fixup and score.
+ */
+int twinkv_score(const twinkv_params* params, const void* keys, const void* values,
+                 int32_t* count, double* best_sim, int32_t* best_idx, double* energy,
+                 double* score, double* omega, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream, hipEvent_t* marks);
+
+/*
+ * twinkv_select - per head g with capacity b = capacity[g] (0 <= b <= N;
+ * values outside are clamped): protect the first s = min(sink, b) and the
+ * last r = min(recent, b - s) positions, then keep the u = b - s - r
+ * unprotected positions ranked first by (score desc, energy desc, position
+ * asc) ([P2] 3.1, 3.2 tie rule, 3.4).
+ *   keep[g][i]  (uint8 [G][N])  1 if retained, else 0
+ *   kept_idx    (int32)         the retained positions of head g in ascending
+ *                               order, at kept_idx[off_g .. off_g + b), where
+ *                               off_g = sum over h < g of clamp(capacity[h]);
+ *                               entries at or beyond kept_idx_len are not written
+ * score, energy: double [G][N] (as produced by twinkv_score; must be finite
+ * and >= 0).  capacity: int32 [G].  Of the parameters only G, N, sink and
+ * recent are read; workspace may be NULL (twinkv_workspace_bytes is 0).
+ * Phases for `marks`: 0 = select.
+ */
+int twinkv_select(const twinkv_params* params, const double* score, const double* energy,
+                  const int32_t* capacity, uint8_t* keep, int32_t* kept_idx, int64_t kept_idx_len,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* marks);
+
+/*
+ * twinkv_repair - one-shot repair of the retained set S0 = {i : keep_in[g][i] != 0}
+ * of every head at its own budget K = |S0| ([P1] section 3.4):
+ *   best_sim[g][i] = b_i(S0) = max over j in S0, |i-j| > window of sim(i,j), or -1
+ *                    (exact fp64 for the chosen j)                       ([P1] Eq. 4)
+ *   best_idx[g][i] = the lowest such j attaining it, or -1
+ *   orphans  O = { i not in S0 : b_i < tau } ranked by (b asc, i asc)
+ *   donors   D = { j in S0 outside the protected regions : b_j >= tau } ranked by
+ *              (b desc, j asc); the protected regions are the first
+ *              min(sink, K) and the last min(recent, K - min(sink, K)) positions
+ *   m = min(|O|, |D|);  S1 = S0 - D[0:m] + O[0:m], so |S1| = |S0|.
+ *   keep_out[g][i]   (uint8 [G][N]) S1
+ *   n_orphans, n_donors, n_swaps: int32 [G]  |O|, |D|, m
+ *   swap_pairs: int32 [G][N/2][2]: (O[k], D[k]) for k < m, then (-1, -1)
+ *     (m <= N/2 always: m <= min(N - K, K)).
+ * keys: bf16 [G][N][d]; keep_in: uint8 [G][N].
+ * Phases for `marks`: 0 = norms, 1 = compaction of S0, 2 = restricted Gram and
+ * fixup, 3 = classification, ranking and swap.
+ */
+int twinkv_repair(const twinkv_params* params, const void* keys, const uint8_t* keep_in,
+                  uint8_t* keep_out, double* best_sim, int32_t* best_idx, int32_t* n_orphans,
+                  int32_t* n_donors, int32_t* n_swaps, int32_t* swap_pairs, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream, hipEvent_t* marks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TWINKV_H */

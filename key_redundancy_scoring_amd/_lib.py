@@ -1,0 +1,293 @@
+"""ctypes binding over libtwinkv.so (the C ABI in include/twinkv.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their data pointers and torch's current HIP stream are handed to
+the library, and every step of the computation runs in the library's HIP
+kernels.  PyTorch provides device memory and the stream; the library never
+allocates.  If the shared library is missing this module raises on use:
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtwinkv.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "twinkv.h")
+
+OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+OP_SCORE, OP_SELECT, OP_REPAIR = 0, 1, 2
+SCORE_PHASES, SELECT_PHASES, REPAIR_PHASES = 2, 1, 4
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("G", ctypes.c_int64),
+        ("N", ctypes.c_int64),
+        ("d", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("tau", ctypes.c_double),
+        ("sink", ctypes.c_int32),
+        ("recent", ctypes.c_int32),
+    ]
+
+
+class TwinKVError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load():
+    """Load libtwinkv.so (built in-tree by ``key_redundancy_scoring_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m key_redundancy_scoring_amd.build` "
+                           "(or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(Params)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    lib.twinkv_workspace_bytes.argtypes = [ctypes.c_int, P]
+    lib.twinkv_workspace_bytes.restype = sz
+    lib.twinkv_uniform_capacity.argtypes = [i64, ctypes.c_double]
+    lib.twinkv_uniform_capacity.restype = i64
+    lib.twinkv_status_string.argtypes = [ctypes.c_int]
+    lib.twinkv_status_string.restype = ctypes.c_char_p
+    lib.twinkv_score.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    lib.twinkv_score.restype = ctypes.c_int
+    lib.twinkv_select.argtypes = [P, vp, vp, vp, vp, vp, i64, vp, sz, vp, vp]
+    lib.twinkv_select.restype = ctypes.c_int
+    lib.twinkv_repair.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    lib.twinkv_repair.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def header_symbols() -> list[str]:
+    """Names of the functions include/twinkv.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(twinkv_[a-z_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return load().twinkv_status_string(int(status)).decode()
+
+
+def params(G, N, d, tau, window, sink=4, recent=64) -> Params:
+    return Params(int(G), int(N), int(d), int(window), float(tau), int(sink), int(recent))
+
+
+def workspace_bytes(op: int, p: Params) -> int:
+    return int(load().twinkv_workspace_bytes(int(op), ctypes.byref(p)))
+
+
+def uniform_capacity(N: int, removal: float) -> int:
+    return int(load().twinkv_uniform_capacity(int(N), float(removal)))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status, where):
+    if status != OK:
+        raise TwinKVError(status, where)
+
+
+def _as_bf16_bits(x, name):
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold bf16 values (torch.bfloat16, or raw bits as int16/uint16)")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if x.dim() != 3:
+        raise ValueError(f"{name} must be [G][N][d]")
+    return x
+
+
+def _need(t, shape, dtype, device, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {device}")
+    return t
+
+
+def _workspace(ws, nbytes, device):
+    if nbytes == 0:
+        return ws
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    return ws
+
+
+def _ws_ptr(ws):
+    if ws is None:
+        return ctypes.c_void_p(0), 0
+    p = ws.data_ptr()
+    aligned = (p + 255) & ~255
+    return ctypes.c_void_p(aligned), ws.numel() - (aligned - p)
+
+
+class Events:
+    """hipEvents created through the HIP runtime, for the optional ``marks``
+    argument (phase timing)."""
+
+    def __init__(self, n: int):
+        hip = ctypes.CDLL("libamdhip64.so")
+        self._hip = hip
+        hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * n)()
+        for k in range(n):
+            e = ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.arr[k] = e.value
+        self.n = n
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        self._hip.hipEventSynchronize(self.arr[b])
+        out = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(out), self.arr[a], self.arr[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self):
+        for k in range(self.n):
+            self._hip.hipEventDestroy(self.arr[k])
+        self.n = 0
+
+
+def _marks(ev: Events | None, phases: int):
+    if ev is None:
+        return ctypes.c_void_p(0)
+    if ev.n < phases + 1:
+        raise ValueError(f"need {phases + 1} events")
+    return ctypes.cast(ev.arr, ctypes.c_void_p)
+
+
+def score(keys, values, tau, window, sink=4, recent=64, omega=False, out=None, ws=None, events=None):
+    """Counts, best nonlocal twin, energy and score for every head.
+
+    keys, values: bf16 [G][N][d] device tensors.  Returns a dict of device
+    tensors: count (int32), best_sim (f64), best_idx (int32), energy (f64),
+    score (f64) and optionally omega (f64), each [G][N], plus the workspace
+    under "ws" for reuse.
+    """
+    lib = load()
+    keys = _as_bf16_bits(keys, "keys")
+    values = _as_bf16_bits(values, "values")
+    if values.shape != keys.shape:
+        raise ValueError("keys and values must have the same shape")
+    G, N, d = keys.shape
+    dev = keys.device
+    p = params(G, N, d, tau, window, sink, recent)
+    out = {} if out is None else out
+    o = {
+        "count": _need(out.get("count"), (G, N), torch.int32, dev, "count"),
+        "best_sim": _need(out.get("best_sim"), (G, N), torch.float64, dev, "best_sim"),
+        "best_idx": _need(out.get("best_idx"), (G, N), torch.int32, dev, "best_idx"),
+        "energy": _need(out.get("energy"), (G, N), torch.float64, dev, "energy"),
+        "score": _need(out.get("score"), (G, N), torch.float64, dev, "score"),
+    }
+    if omega or out.get("omega") is not None:
+        o["omega"] = _need(out.get("omega"), (G, N), torch.float64, dev, "omega")
+    nb = workspace_bytes(OP_SCORE, p)
+    ws = _workspace(ws, nb, dev)
+    wp, wn = _ws_ptr(ws)
+    st = lib.twinkv_score(ctypes.byref(p), _ptr(keys), _ptr(values), _ptr(o["count"]), _ptr(o["best_sim"]),
+                          _ptr(o["best_idx"]), _ptr(o["energy"]), _ptr(o["score"]), _ptr(o.get("omega")), wp, wn,
+                          _stream(), _marks(events, SCORE_PHASES))
+    _check(st, "twinkv_score")
+    o["ws"] = ws
+    return o
+
+
+def capacity_offsets(capacity, N):
+    """Start of each head's run in ``kept_idx`` (host-side; clamped capacities)."""
+    c = torch.as_tensor(capacity).to("cpu", torch.int64).clamp(0, int(N))
+    off = torch.zeros(c.numel() + 1, dtype=torch.int64)
+    off[1:] = torch.cumsum(c, 0)
+    return off
+
+
+def select(score_t, energy_t, capacity, sink=4, recent=64, out=None, events=None):
+    """Exact-budget selection.  ``capacity``: int32 device tensor [G] (or a
+    host sequence, copied to the device).  Returns keep (uint8 [G][N]),
+    kept_idx (int32, heads concatenated, ascending within a head) and the
+    host-side offsets of each head's run."""
+    lib = load()
+    G, N = score_t.shape
+    dev = score_t.device
+    for t, nm in ((score_t, "score"), (energy_t, "energy")):
+        if t.dtype != torch.float64 or not t.is_contiguous() or t.device != dev or tuple(t.shape) != (G, N):
+            raise ValueError(f"{nm} must be contiguous float64 [G][N] on {dev}")
+    if not torch.is_tensor(capacity) or capacity.device != dev:
+        cap_host = torch.as_tensor(capacity, dtype=torch.int32)
+        capacity = cap_host.to(dev)
+    else:
+        cap_host = capacity.to("cpu")
+    if capacity.dtype != torch.int32 or capacity.numel() != G or not capacity.is_contiguous():
+        raise ValueError("capacity must be int32 [G]")
+    off = capacity_offsets(cap_host, N)
+    total = int(off[-1])
+    out = {} if out is None else out
+    keep = _need(out.get("keep"), (G, N), torch.uint8, dev, "keep")
+    kept = out.get("kept_idx")
+    if kept is None or kept.numel() < total:
+        kept = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
+    p = params(G, N, 0, 0.0, 0, sink, recent)  # select reads only G, N, sink, recent
+    st = lib.twinkv_select(ctypes.byref(p), _ptr(score_t), _ptr(energy_t), _ptr(capacity), _ptr(keep), _ptr(kept),
+                           total, ctypes.c_void_p(0), 0, _stream(), _marks(events, SELECT_PHASES))
+    _check(st, "twinkv_select")
+    return {"keep": keep, "kept_idx": kept, "offsets": off, "capacity": capacity}
+
+
+def repair(keys, keep_in, tau, window, sink=4, recent=64, out=None, ws=None, events=None):
+    """One-shot orphan/donor repair of the retained masks ``keep_in`` (uint8
+    [G][N]).  Returns keep (S1), best_sim, best_idx, n_orphans, n_donors,
+    n_swaps and pairs ([G][N//2][2], -1 padded)."""
+    lib = load()
+    keys = _as_bf16_bits(keys, "keys")
+    G, N, d = keys.shape
+    dev = keys.device
+    if keep_in.dtype != torch.uint8 or tuple(keep_in.shape) != (G, N) or not keep_in.is_contiguous() \
+            or keep_in.device != dev:
+        raise ValueError("keep_in must be contiguous uint8 [G][N] on the keys' device")
+    p = params(G, N, d, tau, window, sink, recent)
+    out = {} if out is None else out
+    o = {
+        "keep": _need(out.get("keep"), (G, N), torch.uint8, dev, "keep"),
+        "best_sim": _need(out.get("best_sim"), (G, N), torch.float64, dev, "best_sim"),
+        "best_idx": _need(out.get("best_idx"), (G, N), torch.int32, dev, "best_idx"),
+        "n_orphans": _need(out.get("n_orphans"), (G,), torch.int32, dev, "n_orphans"),
+        "n_donors": _need(out.get("n_donors"), (G,), torch.int32, dev, "n_donors"),
+        "n_swaps": _need(out.get("n_swaps"), (G,), torch.int32, dev, "n_swaps"),
+        "pairs": _need(out.get("pairs"), (G, N // 2, 2), torch.int32, dev, "pairs"),
+    }
+    nb = workspace_bytes(OP_REPAIR, p)
+    ws = _workspace(ws, nb, dev)
+    wp, wn = _ws_ptr(ws)
+    st = lib.twinkv_repair(ctypes.byref(p), _ptr(keys), _ptr(keep_in), _ptr(o["keep"]), _ptr(o["best_sim"]),
+                           _ptr(o["best_idx"]), _ptr(o["n_orphans"]), _ptr(o["n_donors"]), _ptr(o["n_swaps"]),
+                           _ptr(o["pairs"]) if N >= 2 else ctypes.c_void_p(0), wp, wn, _stream(),
+                           _marks(events, REPAIR_PHASES))
+    _check(st, "twinkv_repair")
+    o["ws"] = ws
+    return o

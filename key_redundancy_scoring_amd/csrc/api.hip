@@ -1,0 +1,237 @@
+// C ABI of the key-redundancy scoring library (declared in include/twinkv.h).
+// Host-side argument checks, workspace carving and kernel launches on the
+// caller's stream.  Nothing here allocates device memory.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/twinkv.h"
+#include "internal.h"
+
+namespace {
+
+using namespace twinkv;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Sizes and protection counts, the part of the parameters every op reads.
+int check_sizes(const twinkv_params* p) {
+  if (!p) return TWINKV_ERR_ARG;
+  if (p->G < 1 || p->N < 1 || p->N > (int64_t(1) << 30)) return TWINKV_ERR_ARG;
+  if (p->G > (int64_t(1) << 31) - 1) return TWINKV_ERR_ARG;
+  if (p->sink < 0 || p->recent < 0) return TWINKV_ERR_ARG;
+  return TWINKV_OK;
+}
+
+// Everything the similarity sweep reads as well.
+int check_params(const twinkv_params* p) {
+  const int rc = check_sizes(p);
+  if (rc != TWINKV_OK) return rc;
+  if (p->window < 0) return TWINKV_ERR_ARG;
+  if (!(p->tau > -1.0 && p->tau < 1.0)) return TWINKV_ERR_ARG;  // also rejects NaN
+  if (p->d != 64 && p->d != 128) return TWINKV_ERR_UNSUPPORTED;
+  return TWINKV_OK;
+}
+
+struct Carve {
+  char* base;
+  size_t off = 0;
+  template <class T>
+  T* take(size_t count) {
+    T* r = reinterpret_cast<T*>(base + off);
+    off = align_up(off + count * sizeof(T));
+    return r;
+  }
+};
+
+size_t score_ws(const twinkv_params* p) {
+  const size_t n = (size_t)p->G * (size_t)p->N;
+  return align_up(n * sizeof(double)) + align_up(n * sizeof(float));
+}
+
+size_t repair_ws(const twinkv_params* p) {
+  const size_t n = (size_t)p->G * (size_t)p->N;
+  return align_up(n * sizeof(double)) + align_up(n * sizeof(float)) + align_up(n * sizeof(int32_t)) +
+         align_up((size_t)p->G * sizeof(int32_t)) + 2 * (align_up(n * sizeof(uint64_t)) + align_up(n * sizeof(int32_t)));
+}
+
+int record(hipEvent_t* marks, int k, hipStream_t s) {
+  if (!marks) return TWINKV_OK;
+  return hipEventRecord(marks[k], s) == hipSuccess ? TWINKV_OK : TWINKV_ERR_HIP;
+}
+
+#define TRY_HIP(expr)                                  \
+  do {                                                 \
+    if ((expr) != hipSuccess) return TWINKV_ERR_HIP;   \
+  } while (0)
+#define TRY(expr)                   \
+  do {                              \
+    int _rc = (expr);               \
+    if (_rc != TWINKV_OK) return _rc; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* twinkv_status_string(int status) {
+  switch (status) {
+    case TWINKV_OK: return "ok";
+    case TWINKV_ERR_ARG: return "invalid argument";
+    case TWINKV_ERR_UNSUPPORTED: return "unsupported head dimension (64 or 128 only)";
+    case TWINKV_ERR_WORKSPACE: return "workspace too small";
+    case TWINKV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int64_t twinkv_uniform_capacity(int64_t N, double removal) {
+  if (N < 0 || !(removal >= 0.0 && removal <= 1.0)) return -1;
+  return (int64_t)floor((double)N * (1.0 - removal));
+}
+
+size_t twinkv_workspace_bytes(int op, const twinkv_params* p) {
+  switch (op) {
+    case TWINKV_OP_SCORE: return check_params(p) == TWINKV_OK ? score_ws(p) : 0;
+    case TWINKV_OP_SELECT: return 0;
+    case TWINKV_OP_REPAIR: return check_params(p) == TWINKV_OK ? repair_ws(p) : 0;
+    default: return 0;
+  }
+}
+
+int twinkv_score(const twinkv_params* p, const void* keys, const void* values, int32_t* count, double* best_sim,
+                 int32_t* best_idx, double* energy, double* score, double* omega, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream, hipEvent_t* marks) {
+  TRY(check_params(p));
+  if (!keys || !values || !count || !best_sim || !best_idx || !energy || !score) return TWINKV_ERR_ARG;
+  if (!aligned16(keys) || !aligned16(values)) return TWINKV_ERR_ARG;
+  const size_t need = score_ws(p);
+  if (!workspace || workspace_bytes < need) return TWINKV_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return TWINKV_ERR_ARG;
+
+  Carve cv{static_cast<char*>(workspace)};
+  const size_t n = (size_t)p->G * (size_t)p->N;
+  double* nsq = cv.take<double>(n);
+  float* rinv = cv.take<float>(n);
+
+  TRY(record(marks, 0, stream));
+  TRY_HIP(launch_norms(static_cast<const uint16_t*>(keys), static_cast<const uint16_t*>(values), (int64_t)n, p->d,
+                       nsq, rinv, energy, stream));
+  TRY(record(marks, 1, stream));
+  GramArgs ga{};
+  ga.keys = static_cast<const uint16_t*>(keys);
+  ga.rinv = rinv;
+  ga.nsq = nsq;
+  ga.energy = energy;
+  ga.G = p->G;
+  ga.N = p->N;
+  ga.d = p->d;
+  ga.window = p->window;
+  ga.tau = p->tau;
+  ga.count = count;
+  ga.best_sim = best_sim;
+  ga.best_idx = best_idx;
+  ga.score = score;
+  ga.omega = omega;
+  TRY_HIP(launch_gram(ga, GRAM_SCORE, stream));
+  TRY(record(marks, 2, stream));
+  return TWINKV_OK;
+}
+
+int twinkv_select(const twinkv_params* p, const double* score, const double* energy, const int32_t* capacity,
+                  uint8_t* keep, int32_t* kept_idx, int64_t kept_idx_len, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream, hipEvent_t* marks) {
+  (void)workspace;
+  (void)workspace_bytes;
+  TRY(check_sizes(p));
+  if (!score || !energy || !capacity || !keep) return TWINKV_ERR_ARG;
+  if (kept_idx_len < 0 || (kept_idx_len > 0 && !kept_idx)) return TWINKV_ERR_ARG;
+  SelectArgs sa{};
+  sa.score = score;
+  sa.energy = energy;
+  sa.capacity = capacity;
+  sa.keep = keep;
+  sa.kept_idx = kept_idx;
+  sa.kept_idx_len = kept_idx_len;
+  sa.G = p->G;
+  sa.N = p->N;
+  sa.sink = p->sink;
+  sa.recent = p->recent;
+  TRY(record(marks, 0, stream));
+  TRY_HIP(launch_select(sa, stream));
+  TRY(record(marks, 1, stream));
+  return TWINKV_OK;
+}
+
+int twinkv_repair(const twinkv_params* p, const void* keys, const uint8_t* keep_in, uint8_t* keep_out,
+                  double* best_sim, int32_t* best_idx, int32_t* n_orphans, int32_t* n_donors, int32_t* n_swaps,
+                  int32_t* swap_pairs, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                  hipEvent_t* marks) {
+  TRY(check_params(p));
+  if (!keys || !keep_in || !keep_out || !best_sim || !best_idx || !n_orphans || !n_donors || !n_swaps)
+    return TWINKV_ERR_ARG;
+  if (p->N >= 2 && !swap_pairs) return TWINKV_ERR_ARG;
+  if (!aligned16(keys)) return TWINKV_ERR_ARG;
+  if (keep_in == keep_out) return TWINKV_ERR_ARG;
+  const size_t need = repair_ws(p);
+  if (!workspace || workspace_bytes < need) return TWINKV_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return TWINKV_ERR_ARG;
+
+  Carve cv{static_cast<char*>(workspace)};
+  const size_t n = (size_t)p->G * (size_t)p->N;
+  double* nsq = cv.take<double>(n);
+  float* rinv = cv.take<float>(n);
+  int32_t* pos = cv.take<int32_t>(n);
+  int32_t* ncols = cv.take<int32_t>((size_t)p->G);
+  uint64_t* keys_a = cv.take<uint64_t>(n);
+  int32_t* idx_a = cv.take<int32_t>(n);
+  uint64_t* keys_b = cv.take<uint64_t>(n);
+  int32_t* idx_b = cv.take<int32_t>(n);
+
+  TRY(record(marks, 0, stream));
+  TRY_HIP(launch_norms(static_cast<const uint16_t*>(keys), nullptr, (int64_t)n, p->d, nsq, rinv, nullptr, stream));
+  TRY(record(marks, 1, stream));
+  TRY_HIP(launch_compact(keep_in, p->G, p->N, pos, ncols, stream));
+  TRY(record(marks, 2, stream));
+  GramArgs ga{};
+  ga.keys = static_cast<const uint16_t*>(keys);
+  ga.rinv = rinv;
+  ga.nsq = nsq;
+  ga.pos = pos;
+  ga.ncols = ncols;
+  ga.G = p->G;
+  ga.N = p->N;
+  ga.d = p->d;
+  ga.window = p->window;
+  ga.tau = p->tau;
+  ga.best_sim = best_sim;
+  ga.best_idx = best_idx;
+  TRY_HIP(launch_gram(ga, GRAM_REPAIR, stream));
+  TRY(record(marks, 3, stream));
+  SwapArgs sw{};
+  sw.keep_in = keep_in;
+  sw.best = best_sim;
+  sw.ncols = ncols;
+  sw.keep_out = keep_out;
+  sw.n_orphans = n_orphans;
+  sw.n_donors = n_donors;
+  sw.n_swaps = n_swaps;
+  sw.pairs = swap_pairs;
+  sw.keys_a = keys_a;
+  sw.idx_a = idx_a;
+  sw.keys_b = keys_b;
+  sw.idx_b = idx_b;
+  sw.G = p->G;
+  sw.N = p->N;
+  sw.tau = p->tau;
+  sw.sink = p->sink;
+  sw.recent = p->recent;
+  TRY_HIP(launch_swap(sw, stream));
+  TRY(record(marks, 4, stream));
+  return TWINKV_OK;
+}
+
+}  // extern "C"

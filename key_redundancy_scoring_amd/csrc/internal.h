@@ -1,0 +1,72 @@
+// Internal declarations shared by the library's HIP translation units.
+// Not part of the public ABI (include/twinkv.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace twinkv {
+
+// Column source for the Gram sweep.
+enum GramMode { GRAM_SCORE = 0, GRAM_REPAIR = 1 };
+
+// Rows of one head handled by one workgroup of the Gram kernel.
+constexpr int kGramRowsPerWG = 512;
+
+struct GramArgs {
+  const uint16_t* keys;   // bf16 [G][N][d]
+  const float* rinv;      // 1/||k|| in fp32 [G][N] (0 for a zero key)
+  const double* nsq;      // ||k||^2 in fp64 [G][N]
+  const int32_t* pos;     // repair: retained positions of each head, ascending [G][N]
+  const int32_t* ncols;   // repair: number of retained positions per head [G]
+  const double* energy;   // score: ||v||^2 [G][N]
+  int64_t G, N;
+  int32_t d, window;
+  double tau;
+  // outputs
+  int32_t* count;         // score only
+  double* best_sim;
+  int32_t* best_idx;
+  double* score;          // score only
+  double* omega;          // score only, may be null
+};
+
+hipError_t launch_norms(const uint16_t* keys, const uint16_t* values, int64_t nkeys, int d, double* nsq,
+                        float* rinv, double* energy, hipStream_t stream);
+hipError_t launch_gram(const GramArgs& a, int mode, hipStream_t stream);
+
+struct SelectArgs {
+  const double* score;
+  const double* energy;
+  const int32_t* capacity;
+  uint8_t* keep;
+  int32_t* kept_idx;
+  int64_t kept_idx_len;
+  int64_t G, N;
+  int32_t sink, recent;
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
+hipError_t launch_compact(const uint8_t* keep_in, int64_t G, int64_t N, int32_t* pos, int32_t* ncols,
+                          hipStream_t stream);
+
+struct SwapArgs {
+  const uint8_t* keep_in;
+  const double* best;
+  const int32_t* ncols;  // |S0| per head
+  uint8_t* keep_out;
+  int32_t* n_orphans;
+  int32_t* n_donors;
+  int32_t* n_swaps;
+  int32_t* pairs;        // [G][N/2][2]
+  uint64_t* keys_a;      // workspace [G][N]
+  int32_t* idx_a;        // workspace [G][N]
+  uint64_t* keys_b;      // workspace [G][N]
+  int32_t* idx_b;        // workspace [G][N]
+  int64_t G, N;
+  double tau;
+  int32_t sink, recent;
+};
+hipError_t launch_swap(const SwapArgs& a, hipStream_t stream);
+
+}  // namespace twinkv

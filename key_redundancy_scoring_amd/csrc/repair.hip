@@ -1,0 +1,151 @@
+// Repair-pass kernels ("TwinKV: A Composable Repair Pass for KV Cache Eviction
+// via Pairwise Key Redundancy", section 3.4).
+//
+// compact_kernel: the retained positions of each head in ascending order and
+//   their number K = |S0|; the restricted Gram sweep reads column keys through
+//   this list, so only the K retained columns are compared (the O(nKd) form
+//   the page's complexity section describes).
+//
+// swap_kernel (one 1024-thread workgroup per head), given b_i = b_i(S0):
+//   orphans O = { i not in S0 : b_i < tau }, ranked by (b asc, i asc);
+//   donors  D = { j in S0, outside the sink/recent regions clipped against K :
+//                 b_j >= tau }, ranked by (b desc, j asc);
+//   m = min(|O|, |D|); S1 = S0 - D[:m] + O[:m]; pairs (O[k], D[k]).
+//   Both rankings become "descending 64-bit key, ascending position": the key
+//   is the order-preserving bit image of b for donors and its complement for
+//   orphans.  On the side with more than m members a radix select finds the
+//   m-th key; the m chosen members of each side are gathered in position
+//   order and put in rank order by a stable LSD radix sort, which keeps equal
+//   keys in position order.
+#include "blockops.h"
+
+namespace twinkv {
+namespace {
+
+__global__ __launch_bounds__(kBT) void compact_kernel(const uint8_t* __restrict__ keep_in, int64_t N,
+                                                      int32_t* __restrict__ pos, int32_t* __restrict__ ncols) {
+  __shared__ ScanSmem sc;
+  const int64_t g = blockIdx.x;
+  const uint8_t* in = keep_in + g * N;
+  int32_t* out = pos + g * N;
+  int base = 0;
+  for (int64_t b = 0; b < N; b += kBT) {
+    const int64_t i = b + threadIdx.x;
+    const bool f = i < N && in[i] != 0;
+    int tot = 0;
+    const int r = block_scan_flag(f, sc, &tot);
+    if (f) out[base + r] = (int32_t)i;
+    base += tot;
+  }
+  if (threadIdx.x == 0) ncols[g] = base;
+}
+
+// Gather the top-m members of one side, in position order, into (lk, li).
+template <class KeyOf, class Pred>
+__device__ void collect_side(int64_t N, unsigned m, long long count, KeyOf key_of, Pred pred, uint64_t* lk,
+                             int32_t* li, SelectSmem& ss, ScanSmem& sc) {
+  const bool all = (long long)m == count;
+  uint64_t T = 0;
+  unsigned k_rem = 0, n_eq = 0;
+  if (!all) T = block_radix_select(0, N, m, key_of, pred, ss, &k_rem, &n_eq);
+  int tie_base = 0, base = 0;
+  for (int64_t b = 0; b < N; b += kBT) {
+    const int64_t i = b + threadIdx.x;
+    bool take = false, tie = false;
+    uint64_t key = 0;
+    if (i < N && pred(i)) {
+      key = key_of(i);
+      if (all || key > T) take = true;
+      else if (key == T) tie = true;
+    }
+    int tt = 0;
+    const int tr = block_scan_flag(tie, sc, &tt);
+    if (tie && (unsigned)(tie_base + tr) < k_rem) take = true;
+    tie_base += tt;
+    int kt = 0;
+    const int kr = block_scan_flag(take, sc, &kt);
+    if (take) {
+      lk[base + kr] = key;
+      li[base + kr] = (int32_t)i;
+    }
+    base += kt;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kBT) void swap_kernel(SwapArgs a) {
+  __shared__ SelectSmem ss;
+  __shared__ ScanSmem sc;
+  __shared__ SortSmem so;
+  __shared__ long long red[kBW];
+
+  const int64_t g = blockIdx.x;
+  const int64_t N = a.N;
+  const int64_t K = a.ncols[g];
+  const int64_t s_cnt = a.sink < K ? a.sink : K;
+  const int64_t r_cnt = a.recent < K - s_cnt ? a.recent : K - s_cnt;
+  const uint8_t* in = a.keep_in + g * N;
+  const double* bs = a.best + g * N;
+  uint8_t* out = a.keep_out + g * N;
+  const double tau = a.tau;
+
+  auto is_orphan = [&](int64_t i) { return in[i] == 0 && bs[i] < tau; };
+  auto is_donor = [&](int64_t i) { return in[i] != 0 && i >= s_cnt && i < N - r_cnt && bs[i] >= tau; };
+  auto orphan_key = [&](int64_t i) { return ~ordered_bits(bs[i]); };
+  auto donor_key = [&](int64_t i) { return ordered_bits(bs[i]); };
+
+  long long no = 0, nd = 0;
+  for (int64_t i = threadIdx.x; i < N; i += kBT) {
+    no += is_orphan(i) ? 1 : 0;
+    nd += is_donor(i) ? 1 : 0;
+    out[i] = in[i] != 0 ? 1 : 0;
+  }
+  no = block_sum(no, red);
+  nd = block_sum(nd, red);
+  const long long m = no < nd ? no : nd;
+  __syncthreads();
+
+  int32_t* pairs = a.pairs + g * (N / 2) * 2;
+  if (m > 0) {
+    uint64_t* ka = a.keys_a + g * N;
+    int32_t* ia = a.idx_a + g * N;
+    uint64_t* kb = a.keys_b + g * N;
+    int32_t* ib = a.idx_b + g * N;
+    collect_side(N, (unsigned)m, no, orphan_key, is_orphan, ka, ia, ss, sc);
+    collect_side(N, (unsigned)m, nd, donor_key, is_donor, ka + m, ia + m, ss, sc);
+    block_sort_desc(ka, ia, kb, ib, (int)m, so);
+    block_sort_desc(ka + m, ia + m, kb + m, ib + m, (int)m, so);
+    for (int64_t k = threadIdx.x; k < m; k += kBT) {
+      const int32_t o = ia[k];
+      const int32_t dn = ia[m + k];
+      out[dn] = 0;
+      out[o] = 1;
+      pairs[2 * k] = o;
+      pairs[2 * k + 1] = dn;
+    }
+  }
+  for (int64_t k = m + threadIdx.x; k < N / 2; k += kBT) {
+    pairs[2 * k] = -1;
+    pairs[2 * k + 1] = -1;
+  }
+  if (threadIdx.x == 0) {
+    a.n_orphans[g] = (int32_t)no;
+    a.n_donors[g] = (int32_t)nd;
+    a.n_swaps[g] = (int32_t)m;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_compact(const uint8_t* keep_in, int64_t G, int64_t N, int32_t* pos, int32_t* ncols,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL(compact_kernel, dim3((unsigned)G), dim3(kBT), 0, stream, keep_in, N, pos, ncols);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap(const SwapArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(swap_kernel, dim3((unsigned)a.G), dim3(kBT), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace twinkv

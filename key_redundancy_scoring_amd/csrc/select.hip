@@ -1,0 +1,121 @@
+// Exact-budget per-head selection ("Small Frequency Corrections Can Change
+// What Survives KV Cache Compression", sections 3.1, 3.2 and 3.4):
+// keep the protected sinks and recent positions, clipped against the head's
+// capacity (sinks first), and the u = b - s - r unprotected positions ranked
+// first by (score desc, energy desc, position asc).
+//
+// One 1024-thread workgroup per head.  Scores and energies are non-negative
+// fp64, so their bit patterns order like the values.  An MSB-first radix
+// select (8 passes of 8-bit digits) finds the u-th largest score; only if the
+// boundary value is shared by more positions than remain to be taken does a
+// second select run on the energies of those ties, and only if that boundary
+// is shared too are the remaining slots given to the lowest positions.  A
+// final pass in position order writes the keep mask and the ascending list of
+// retained positions.
+#include "blockops.h"
+
+namespace twinkv {
+namespace {
+
+__device__ __forceinline__ uint64_t dbits(double x) { return (uint64_t)__double_as_longlong(x + 0.0); }
+
+__global__ __launch_bounds__(kBT) void select_kernel(SelectArgs a) {
+  __shared__ SelectSmem ss;
+  __shared__ ScanSmem sc;
+  __shared__ long long red[kBW];
+
+  const int64_t g = blockIdx.x;
+  const int64_t N = a.N;
+  const double* sc_g = a.score + g * N;
+  const double* en_g = a.energy + g * N;
+
+  int64_t cap = a.capacity[g];
+  cap = cap < 0 ? 0 : (cap > N ? N : cap);
+  const int64_t s_cnt = a.sink < cap ? a.sink : cap;
+  const int64_t r_cnt = a.recent < cap - s_cnt ? a.recent : cap - s_cnt;
+  const int64_t u = cap - s_cnt - r_cnt;
+  const int64_t lo = s_cnt, hi = N - r_cnt;  // unprotected candidates [lo, hi)
+
+  // offset of this head's list: sum of clamped capacities of the heads before it
+  long long part = 0;
+  for (int64_t q = threadIdx.x; q < g; q += kBT) {
+    long long c = a.capacity[q];
+    part += c < 0 ? 0 : (c > N ? N : c);
+  }
+  const long long off_g = block_sum(part, red);
+
+  // level 0: take no candidate; 1: all; 2: score > T1, ties resolved below
+  int level;
+  uint64_t T1 = 0, T2 = 0;
+  unsigned k1 = 0, k2 = 0, n1 = 0, n2 = 0;
+  bool lvl_energy = false, lvl_index = false;
+  if (u == 0) {
+    level = 0;
+  } else if (u == hi - lo) {
+    level = 1;
+  } else {
+    level = 2;
+    T1 = block_radix_select(
+        lo, hi, (unsigned)u, [&](int64_t i) { return dbits(sc_g[i]); }, [](int64_t) { return true; }, ss, &k1, &n1);
+    if (k1 < n1) {
+      lvl_energy = true;
+      T2 = block_radix_select(
+          lo, hi, k1, [&](int64_t i) { return dbits(en_g[i]); }, [&](int64_t i) { return dbits(sc_g[i]) == T1; }, ss,
+          &k2, &n2);
+      lvl_index = k2 < n2;
+    }
+  }
+
+  // final pass in position order
+  int tie_base = 0, kept_base = 0;
+  for (int64_t base = 0; base < N; base += kBT) {
+    const int64_t i = base + threadIdx.x;
+    const bool in = i < N;
+    const bool prot = in && (i < lo || i >= hi);
+    const bool cand = in && !prot;
+    bool take = prot;
+    bool tie = false;
+    if (cand) {
+      if (level == 1) {
+        take = true;
+      } else if (level == 2) {
+        const uint64_t s1 = dbits(sc_g[i]);
+        if (s1 > T1) {
+          take = true;
+        } else if (s1 == T1) {
+          if (!lvl_energy) {
+            take = true;
+          } else {
+            const uint64_t e1 = dbits(en_g[i]);
+            if (e1 > T2) take = true;
+            else if (e1 == T2) {
+              if (!lvl_index) take = true;
+              else tie = true;
+            }
+          }
+        }
+      }
+    }
+    int tie_tot = 0;
+    const int trank = block_scan_flag(tie, sc, &tie_tot);
+    if (tie && (unsigned)(tie_base + trank) < k2) take = true;
+    tie_base += tie_tot;
+    int kept_tot = 0;
+    const int krank = block_scan_flag(take, sc, &kept_tot);
+    if (in) a.keep[g * N + i] = take ? 1 : 0;
+    if (take) {
+      const long long dst = off_g + kept_base + krank;
+      if (dst < a.kept_idx_len) a.kept_idx[dst] = (int32_t)i;
+    }
+    kept_base += kept_tot;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.G), dim3(kBT), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace twinkv

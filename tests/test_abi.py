@@ -1,0 +1,108 @@
+"""The C-ABI library: it loads, exports every function the header declares,
+and its host-side checks reject bad arguments before any launch.  No call in
+this file reaches a kernel launch, so it runs without a GPU."""
+import ctypes
+import subprocess
+
+import pytest
+
+import key_redundancy_scoring_amd as krs
+from key_redundancy_scoring_amd import _lib as L
+from oracle import twinkv_oracle as O
+
+FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: every call below fails validation first
+
+
+def test_library_exports_every_header_symbol():
+    lib = krs.load()
+    declared = krs.header_symbols()
+    assert declared == ["twinkv_repair", "twinkv_score", "twinkv_select", "twinkv_status_string",
+                        "twinkv_uniform_capacity", "twinkv_workspace_bytes"]
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(declared) <= exported
+
+
+def test_status_strings():
+    for st in (L.OK, L.ERR_ARG, L.ERR_UNSUPPORTED, L.ERR_WORKSPACE, L.ERR_HIP):
+        assert krs.status_string(st) != "unknown status"
+    assert krs.status_string(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("N,r", [(172, 0.75), (512, 0.5), (8192, 0.7), (32768, 0.5), (131072, 0.75), (10, 0.35),
+                                 (7, 0.0), (7, 1.0), (1000, 0.3)])
+def test_uniform_capacity_matches_oracle(N, r):
+    assert krs.uniform_capacity(N, r) == O.uniform_budget(N, r)
+
+
+def test_uniform_capacity_rejects():
+    assert krs.uniform_capacity(-1, 0.5) == -1
+    assert krs.uniform_capacity(10, 1.5) == -1
+    assert krs.uniform_capacity(10, float("nan")) == -1
+
+
+def test_workspace_sizes():
+    p = krs.params(128, 32768, 64, 0.9, 64)
+    n = 128 * 32768
+    assert krs.workspace_bytes(L.OP_SCORE, p) >= n * 12
+    assert krs.workspace_bytes(L.OP_SELECT, p) == 0
+    assert krs.workspace_bytes(L.OP_REPAIR, p) >= n * 40
+    assert krs.workspace_bytes(L.OP_SCORE, krs.params(1, 10, 96, 0.9, 4)) == 0  # unsupported d
+    assert krs.workspace_bytes(7, p) == 0
+
+
+def _score_call(p, ws_bytes=1 << 30, keys=FAKE, values=FAKE, ws=FAKE):
+    lib = krs.load()
+    return lib.twinkv_score(ctypes.byref(p) if p is not None else None, keys, values, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            None, ws, ws_bytes, None, None)
+
+
+def test_score_validation():
+    good = krs.params(2, 100, 64, 0.9, 8)
+    assert _score_call(None) == L.ERR_ARG
+    assert _score_call(krs.params(2, 100, 96, 0.9, 8)) == L.ERR_UNSUPPORTED
+    assert _score_call(krs.params(0, 100, 64, 0.9, 8)) == L.ERR_ARG
+    assert _score_call(krs.params(2, 0, 64, 0.9, 8)) == L.ERR_ARG
+    assert _score_call(krs.params(2, (1 << 30) + 1, 64, 0.9, 8)) == L.ERR_ARG
+    assert _score_call(krs.params(2, 100, 64, 1.0, 8)) == L.ERR_ARG
+    assert _score_call(krs.params(2, 100, 64, -1.0, 8)) == L.ERR_ARG
+    assert _score_call(krs.params(2, 100, 64, float("nan"), 8)) == L.ERR_ARG
+    assert _score_call(krs.params(2, 100, 64, 0.9, -1)) == L.ERR_ARG
+    assert _score_call(krs.params(2, 100, 64, 0.9, 8, sink=-1)) == L.ERR_ARG
+    assert _score_call(good, keys=None) == L.ERR_ARG
+    assert _score_call(good, keys=ctypes.c_void_p(0x100002)) == L.ERR_ARG  # misaligned
+    assert _score_call(good, ws_bytes=16) == L.ERR_WORKSPACE
+    assert _score_call(good, ws=None) == L.ERR_WORKSPACE
+    assert _score_call(good, ws=ctypes.c_void_p(0x100010)) == L.ERR_ARG  # workspace not 256-byte aligned
+
+
+def test_select_validation():
+    lib = krs.load()
+    p = krs.params(2, 100, 0, 0.0, 0)  # select ignores d, tau and window
+    call = lambda p, kept=FAKE, n=10, keep=FAKE: lib.twinkv_select(  # noqa: E731
+        ctypes.byref(p) if p is not None else None, FAKE, FAKE, FAKE, keep, kept, n, None, 0, None, None)
+    assert call(None) == L.ERR_ARG
+    assert call(krs.params(2, 0, 0, 0.0, 0)) == L.ERR_ARG
+    assert call(p, keep=None) == L.ERR_ARG
+    assert call(p, kept=None, n=5) == L.ERR_ARG
+    assert call(p, n=-1) == L.ERR_ARG
+
+
+def test_repair_validation():
+    lib = krs.load()
+    call = lambda p, keep_out=FAKE, pairs=FAKE, ws=FAKE, nb=1 << 30: lib.twinkv_repair(  # noqa: E731
+        ctypes.byref(p), FAKE, FAKE, keep_out, FAKE, FAKE, FAKE, FAKE, FAKE, pairs, ws, nb, None, None)
+    good = krs.params(2, 100, 128, 0.9, 8)
+    assert call(krs.params(2, 100, 32, 0.9, 8)) == L.ERR_UNSUPPORTED
+    assert call(good, keep_out=None) == L.ERR_ARG
+    assert call(good, keep_out=FAKE) == L.ERR_ARG  # keep_out aliases keep_in
+    assert call(good, keep_out=ctypes.c_void_p(0x200000), pairs=None) == L.ERR_ARG
+    assert call(good, keep_out=ctypes.c_void_p(0x200000), nb=100) == L.ERR_WORKSPACE
+
+
+def test_params_struct_layout():
+    assert ctypes.sizeof(L.Params) == 40
+    assert [L.Params.G.offset, L.Params.N.offset, L.Params.d.offset, L.Params.window.offset, L.Params.tau.offset,
+            L.Params.sink.offset, L.Params.recent.offset] == [0, 8, 16, 20, 24, 32, 36]

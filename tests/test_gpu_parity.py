@@ -1,0 +1,231 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on
+the same seeded inputs, element by element, at sizes the oracle finishes in
+seconds that still span several workgroups, LDS stages and ragged tails;
+plus the degenerate cases.  Full-size workloads live in test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import key_redundancy_scoring_amd as krs
+from oracle import twinkv_oracle as O
+from synth import dirichlet_capacities, get_config, gumbel_retained, make_heads
+from tests import parity as PR
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return torch.device("cuda:0")
+
+
+def _up(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(_dev())
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _score_numpy(res, g):
+    return {k: res[k][g].cpu().numpy() for k in ("count", "best_sim", "best_idx", "energy", "score", "omega")
+            if k in res} | {"best": res["best_sim"][g].cpu().numpy(), "arg": res["best_idx"][g].cpu().numpy()}
+
+
+def _run_score_select_repair(K, V, cfg, caps, do_repair_on_select=False, tag=""):
+    """Score + select (+ repair of the select output) on the GPU and check every
+    head against the oracle."""
+    G, N, d = K.shape
+    _say(f"[{tag}] score G={G} N={N} d={d}")
+    tk, tv = _up(K), _up(V)
+    res = krs.score(tk, tv, cfg.tau, cfg.window, cfg.sink, cfg.recent, omega=True)
+    sel = krs.select(res["score"], res["energy"], torch.tensor(caps, dtype=torch.int32, device=_dev()),
+                     cfg.sink, cfg.recent)
+    rep_res = None
+    if do_repair_on_select:
+        rep_res = krs.repair(tk, sel["keep"], cfg.tau, cfg.window, cfg.sink, cfg.recent)
+    torch.cuda.synchronize()
+    keep = sel["keep"].cpu().numpy()
+    kept = sel["kept_idx"].cpu().numpy()
+    off = sel["offsets"].numpy()
+    reports = []
+    for g in range(G):
+        ref = PR.score_reference(K[g], V[g], cfg.tau, cfg.window)
+        gpu = _score_numpy(res, g)
+        r = PR.compare_score(gpu, ref, tag=f"{tag} head {g}")
+        cap = int(caps[g])
+        okeep, oidx = O.select_head(ref["score"], ref["energy"], cap, cfg.sink, cfg.recent)
+        exact = r["band_rows"] == 0 and PR.boundary_gap(ref["score"], ref["energy"], cap, cfg.sink,
+                                                         cfg.recent) >= PR.BOUNDARY_GAP
+        PR.check_select_properties(keep[g], kept[off[g]:off[g + 1]], gpu["score"], gpu["energy"], cap, cfg.sink,
+                                   cfg.recent, tag=f"{tag} head {g}")
+        if exact:
+            np.testing.assert_array_equal(keep[g], okeep, err_msg=f"{tag} head {g} keep")
+            np.testing.assert_array_equal(kept[off[g]:off[g + 1]], oidx, err_msg=f"{tag} head {g} kept_idx")
+        r["select_exact"] = exact
+        if rep_res is not None and exact:
+            rref = PR.repair_reference(K[g], okeep, cfg.tau, cfg.window, cfg.sink, cfg.recent)
+            rg = {k: rep_res[k][g].cpu().numpy() for k in ("keep", "n_orphans", "n_donors", "n_swaps", "pairs")}
+            rg["best"] = rep_res["best_sim"][g].cpu().numpy()
+            rg["arg"] = rep_res["best_idx"][g].cpu().numpy()
+            r["repair"] = PR.compare_repair(rg, rref, okeep, cfg.tau, tag=f"{tag} head {g} repair")
+        reports.append(r)
+    _say(f"[{tag}] ok", reports[:2])
+    return res, sel, reports
+
+
+def test_tiny_config_full():
+    cfg = get_config(1)
+    K, V, _ = make_heads(cfg)
+    caps = [O.uniform_budget(cfg.N, cfg.removal)] * cfg.G
+    _run_score_select_repair(K, V, cfg, caps, do_repair_on_select=True, tag="cfg1")
+
+
+@pytest.mark.parametrize("cfg_id,G,N", [(2, 3, 1500), (2, 2, 513), (2, 1, 65), (4, 2, 1100), (3, 2, 700)])
+def test_score_select_ragged(cfg_id, G, N):
+    cfg = get_config(cfg_id)
+    K, V, _ = make_heads(cfg, heads=range(G), N=N)
+    r = cfg.removal if cfg.removal is not None else 0.5
+    caps = [O.uniform_budget(N, r)] * G
+    _run_score_select_repair(K, V, cfg, caps, do_repair_on_select=True, tag=f"cfg{cfg_id} G{G} N{N}")
+
+
+def test_dirichlet_capacities_small():
+    cfg = get_config(5)
+    G, N = 16, 900
+    K, V, _ = make_heads(cfg, heads=range(G), N=N)
+    caps = dirichlet_capacities(cfg, G=G, N=N)
+    _run_score_select_repair(K, V, cfg, caps, do_repair_on_select=True, tag="cfg5 small")
+
+
+@pytest.mark.parametrize("N", [1300, 257])
+def test_repair_gumbel_small(N):
+    cfg = get_config(3)
+    G = 3
+    _say(f"[repair gumbel N={N}]")
+    K, _, _ = make_heads(cfg, heads=range(G), N=N, with_values=False)
+    S0 = np.stack([gumbel_retained(cfg, g, N=N) for g in range(G)])
+    res = krs.repair(_up(K), torch.from_numpy(S0).to(_dev()), cfg.tau, cfg.window, cfg.sink, cfg.recent)
+    torch.cuda.synchronize()
+    for g in range(G):
+        rref = PR.repair_reference(K[g], S0[g], cfg.tau, cfg.window, cfg.sink, cfg.recent)
+        rg = {k: res[k][g].cpu().numpy() for k in ("keep", "n_orphans", "n_donors", "n_swaps", "pairs")}
+        rg["best"] = res["best_sim"][g].cpu().numpy()
+        rg["arg"] = res["best_idx"][g].cpu().numpy()
+        rep = PR.compare_repair(rg, rref, S0[g], cfg.tau, tag=f"gumbel head {g}")
+        assert rep["bit_exact_inputs"]
+        assert rref["m"] > 0  # the case exercises real swaps
+
+
+# ---------------------------------------------------------------------------
+# degenerate cases
+
+
+def _bf16(x):
+    from synth import f64_to_bf16_bits
+    return f64_to_bf16_bits(np.asarray(x, dtype=np.float64))
+
+
+def _score_one(K, V, tau, window, sink=4, recent=8):
+    res = krs.score(_up(K), _up(V), tau, window, sink, recent, omega=True)
+    torch.cuda.synchronize()
+    return res
+
+
+@pytest.mark.parametrize("N,w", [(1, 0), (2, 1), (33, 32), (34, 32), (5, 0)])
+def test_few_positions(N, w):
+    rng = np.random.default_rng(N)
+    K = _bf16(rng.standard_normal((2, N, 64)))
+    V = _bf16(rng.standard_normal((2, N, 64)))
+    _say(f"[few N={N} w={w}]")
+    res = _score_one(K, V, 0.5, w)
+    for g in range(2):
+        ref = PR.score_reference(K[g], V[g], 0.5, w)
+        PR.compare_score(_score_numpy(res, g), ref, tag=f"few N={N} head {g}")
+    for cap in (0, N // 2, N):
+        sel = krs.select(res["score"], res["energy"], [cap, cap], 1, 1)
+        torch.cuda.synchronize()
+        for g in range(2):
+            ok, oi = O.select_head(res["score"][g].cpu().numpy(), res["energy"][g].cpu().numpy(), cap, 1, 1)
+            np.testing.assert_array_equal(sel["keep"][g].cpu().numpy(), ok)
+
+
+def test_identical_and_zero_keys_tie_rules():
+    N, d = 700, 64
+    rng = np.random.default_rng(1)
+    Kf = rng.standard_normal((1, N, d))
+    Kf[0, 100:700:50] = Kf[0, 50]  # exact copies of key 50 at 100, 150, ...: sim exactly 1, exact ties
+    Kf[0, 300] = 0.0  # a zero key
+    Kf[0, 301] = 0.0
+    K = _bf16(Kf)
+    V = _bf16(np.ones((1, N, d)))  # equal energies: the tie rule falls through to positions
+    _say("[identical keys]")
+    for tau in (0.9, -0.5):
+        res = _score_one(K, V, tau, 16)
+        ref = PR.score_reference(K[0], V[0], tau, 16)
+        PR.compare_score(_score_numpy(res, 0), ref, tag=f"identical tau={tau}")
+        a = res["best_idx"][0].cpu().numpy()
+        assert a[50] == 100 and a[650] == 50
+        sel = krs.select(res["score"], res["energy"], [350], 4, 8)
+        torch.cuda.synchronize()
+        ok, oi = O.select_head(ref["score"], ref["energy"], 350, 4, 8)
+        np.testing.assert_array_equal(sel["keep"][0].cpu().numpy(), ok)
+
+
+def test_all_zero_values_select_by_position():
+    N = 300
+    rng = np.random.default_rng(2)
+    K = _bf16(rng.standard_normal((1, N, 128)))
+    V = np.zeros((1, N, 128), np.uint16)
+    res = _score_one(K, V, 0.9, 8)
+    sel = krs.select(res["score"], res["energy"], [100], 4, 8)
+    torch.cuda.synchronize()
+    idx = sel["kept_idx"].cpu().numpy()
+    assert idx.tolist() == list(range(4 + 88)) + list(range(N - 8, N))
+
+
+def test_capacity_edges_and_clamping():
+    cfg = get_config(2)
+    G, N = 6, 400
+    K, V, _ = make_heads(cfg, heads=range(G), N=N)
+    res = krs.score(_up(K), _up(V), cfg.tau, cfg.window, 4, 64)
+    caps = [0, 3, 40, 67, 68, N]
+    sel = krs.select(res["score"], res["energy"], caps, 4, 64)
+    torch.cuda.synchronize()
+    keep = sel["keep"].cpu().numpy()
+    off = sel["offsets"].numpy()
+    for g in range(G):
+        ok, oi = O.select_head(res["score"][g].cpu().numpy(), res["energy"][g].cpu().numpy(), caps[g], 4, 64)
+        np.testing.assert_array_equal(keep[g], ok)
+        np.testing.assert_array_equal(sel["kept_idx"].cpu().numpy()[off[g]:off[g + 1]], oi)
+
+
+def test_repair_noop_and_extremes():
+    cfg = get_config(3)
+    G, N = 4, 600
+    K, _, _ = make_heads(cfg, heads=range(G), N=N, with_values=False)
+    masks = np.zeros((G, N), np.uint8)
+    masks[1] = 1  # keep everything: no orphans
+    masks[2, ::2] = 1
+    masks[3, :5] = 1
+    res = krs.repair(_up(K), torch.from_numpy(masks).to(_dev()), cfg.tau, cfg.window, cfg.sink, cfg.recent)
+    torch.cuda.synchronize()
+    for g in range(G):
+        rref = PR.repair_reference(K[g], masks[g], cfg.tau, cfg.window, cfg.sink, cfg.recent)
+        rg = {k: res[k][g].cpu().numpy() for k in ("keep", "n_orphans", "n_donors", "n_swaps", "pairs")}
+        rg["best"] = res["best_sim"][g].cpu().numpy()
+        rg["arg"] = res["best_idx"][g].cpu().numpy()
+        PR.compare_repair(rg, rref, masks[g], cfg.tau, tag=f"extreme head {g}")
+    assert int(res["n_swaps"][0]) == 0 and int(res["n_swaps"][1]) == 0
+
+
+def test_deterministic_repeat():
+    cfg = get_config(2)
+    K, V, _ = make_heads(cfg, heads=range(4), N=2000)
+    tk, tv = _up(K), _up(V)
+    a = krs.score(tk, tv, cfg.tau, cfg.window, omega=True)
+    b = krs.score(tk, tv, cfg.tau, cfg.window, omega=True)
+    torch.cuda.synchronize()
+    for k in ("count", "best_sim", "best_idx", "energy", "score", "omega"):
+        assert torch.equal(a[k], b[k]), k
