@@ -150,8 +150,9 @@ int twinkv_select(const twinkv_params* params, const double* score, const double
  *   swap_pairs: int32 [G][N/2][2]: (O[k], D[k]) for k < m, then (-1, -1)
  *     (m <= N/2 always: m <= min(N - K, K)).
  * keys: bf16 [G][N][d]; keep_in: uint8 [G][N].
- * Phases for `marks`: 0 = norms, 1 = compaction of S0, 2 = restricted Gram and
- * fixup, 3 = classification, ranking and swap.
+ * Phases for `marks`: 0 = norms, 1 = compaction of S0 (retained positions and a
+ * contiguous copy of their keys), 2 = restricted Gram and fixup,
+ * 3 = classification, ranking and swap.
  */
 int twinkv_repair(const twinkv_params* params, const void* keys, const uint8_t* keep_in,
                   uint8_t* keep_out, double* best_sim, int32_t* best_idx, int32_t* n_orphans,

@@ -36,6 +36,12 @@ COMMON = [
 ]
 
 
+# Gram sweep: MFMA results go straight to VGPRs, where the epilogue reads them,
+# instead of AGPRs that would need a copy per accumulator; its inputs are finite
+# (no NaN), so max trees need no NaN-quieting copies (infinities stay honoured).
+PER_SOURCE = {"gram.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
+
+
 def _hipcc() -> str:
     exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(exe):
@@ -52,27 +58,32 @@ def _run(cmd):
     return err
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
+def build(verbose: bool = False, jobs: int | None = None, defines: dict | None = None, out: str | None = None) -> str:
+    """Compile and link the library; ``defines`` adds -D macros (tile shapes),
+    ``out`` writes the library somewhere other than the package directory."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    lib = out or LIB
+    bdir = BUILD_DIR if out is None else os.path.join(os.path.dirname(os.path.abspath(out)), "_build")
+    os.makedirs(bdir, exist_ok=True)
+    dflags = [f"-D{k}={v}" for k, v in (defines or {}).items()]
     objs = []
     cmds = []
     for s in SOURCES:
         src = os.path.join(CSRC, s)
-        obj = os.path.join(BUILD_DIR, s.replace(".hip", ".o"))
+        obj = os.path.join(bdir, s.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc, *COMMON, "-c", src, "-o", obj])
+        cmds.append([hipcc, *COMMON, *PER_SOURCE.get(s, []), *dflags, "-c", src, "-o", obj])
     jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 2)))
     with cf.ThreadPoolExecutor(jobs) as ex:
         for cmd, err in zip(cmds, ex.map(_run, cmds)):
             if verbose and err.strip():
                 print(err, file=sys.stderr)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":

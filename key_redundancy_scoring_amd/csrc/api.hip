@@ -4,7 +4,7 @@
 #include <math.h>
 #include <string.h>
 
-#include "../../include/twinkv.h"
+#include "twinkv.h"
 #include "internal.h"
 
 namespace {
@@ -55,7 +55,8 @@ size_t score_ws(const twinkv_params* p) {
 size_t repair_ws(const twinkv_params* p) {
   const size_t n = (size_t)p->G * (size_t)p->N;
   return align_up(n * sizeof(double)) + align_up(n * sizeof(float)) + align_up(n * sizeof(int32_t)) +
-         align_up((size_t)p->G * sizeof(int32_t)) + 2 * (align_up(n * sizeof(uint64_t)) + align_up(n * sizeof(int32_t)));
+         align_up((size_t)p->G * sizeof(int32_t)) + 2 * (align_up(n * sizeof(uint64_t)) + align_up(n * sizeof(int32_t))) +
+         align_up(n * (size_t)p->d * sizeof(uint16_t)) + align_up(n * sizeof(float));
 }
 
 int record(hipEvent_t* marks, int k, hipStream_t s) {
@@ -123,8 +124,9 @@ int twinkv_score(const twinkv_params* p, const void* keys, const void* values, i
   TRY(record(marks, 1, stream));
   GramArgs ga{};
   ga.keys = static_cast<const uint16_t*>(keys);
-  ga.rinv = rinv;
   ga.nsq = nsq;
+  ga.col_keys = ga.keys;
+  ga.col_rinv = rinv;
   ga.energy = energy;
   ga.G = p->G;
   ga.N = p->N;
@@ -190,17 +192,22 @@ int twinkv_repair(const twinkv_params* p, const void* keys, const uint8_t* keep_
   int32_t* idx_a = cv.take<int32_t>(n);
   uint64_t* keys_b = cv.take<uint64_t>(n);
   int32_t* idx_b = cv.take<int32_t>(n);
+  uint16_t* ckeys = cv.take<uint16_t>(n * (size_t)p->d);
+  float* crinv = cv.take<float>(n);
+  const uint16_t* kin = static_cast<const uint16_t*>(keys);
 
   TRY(record(marks, 0, stream));
-  TRY_HIP(launch_norms(static_cast<const uint16_t*>(keys), nullptr, (int64_t)n, p->d, nsq, rinv, nullptr, stream));
+  TRY_HIP(launch_norms(kin, nullptr, (int64_t)n, p->d, nsq, rinv, nullptr, stream));
   TRY(record(marks, 1, stream));
   TRY_HIP(launch_compact(keep_in, p->G, p->N, pos, ncols, stream));
+  TRY_HIP(launch_gather(kin, rinv, pos, ncols, p->G, p->N, p->d, ckeys, crinv, stream));
   TRY(record(marks, 2, stream));
   GramArgs ga{};
-  ga.keys = static_cast<const uint16_t*>(keys);
-  ga.rinv = rinv;
+  ga.keys = kin;
   ga.nsq = nsq;
-  ga.pos = pos;
+  ga.col_keys = ckeys;
+  ga.col_rinv = crinv;
+  ga.col_pos = pos;
   ga.ncols = ncols;
   ga.G = p->G;
   ga.N = p->N;

@@ -11,21 +11,34 @@
 // never written anywhere.
 //
 // Mapping onto gfx950:
-//   * A workgroup is 4 waves and owns 512 consecutive rows of one head; each
-//     wave owns 4 blocks of 32 rows whose bf16 keys stay in VGPRs as MFMA
-//     B operands for the whole sweep.
-//   * Column keys stream through LDS in stages of 64 columns (double
-//     buffered, one barrier per stage).  16-byte chunks are XOR-swizzled by
-//     the column's low 3 bits so the MFMA A-operand reads are spread over banks.
+//   * A workgroup of WAVES waves owns WAVES*RB*32 consecutive rows of one head;
+//     each wave owns RB blocks of 32 rows whose bf16 keys stay in VGPRs as
+//     MFMA B operands for the whole sweep.  Two workgroups share a CU, so one
+//     workgroup's prologue and fp64 fixup overlap the other's sweep.
+//   * Column keys stream HBM/L2 -> LDS in stages of SC columns with
+//     global_load_lds (no VGPR round trip), into two LDS buffers: stage s+1
+//     is in flight while stage s is computed, and the one wait per stage sits
+//     before the barrier.  Columns are contiguous rows of a key array: the
+//     head's own keys in score mode, a compacted copy of the retained keys in
+//     repair mode.  Each lane of a direct load writes 16 bytes at
+//     base + 16*lane, so the XOR swizzle that spreads the MFMA A-operand reads
+//     over the LDS banks (16-byte chunk k of column c sits at slot
+//     c*CH + (k ^ (c & 7))) is applied by choosing which global chunk each
+//     lane fetches.  Columns past the end are clamped to the last one; the
+//     tiles that hold them are handled by the masked path below.
 //   * v_mfma_f32_32x32x16_bf16 with A = 32 column keys, B = 32 row keys gives
 //     lane l the row (l mod 32) and 16 columns 8*(r/4) + 4*(l/32) + (r mod 4)
 //     in accumulator r, so all reductions over columns stay inside a lane.
-//   * Epilogue per 32x32 tile and lane: y = dot * (1/||k_j||) (16 mul), the
-//     tile maximum by a 3-input max tree (8 ops), then one compare and two
-//     selects record (running max, tile index).  The count needs y > tau*||k_i||
-//     and runs only when the tile maximum crosses that threshold (rare: twins
-//     are sparse).  The |i-j| <= w band and the ragged tail take a masked
-//     variant on the few tiles that touch them.
+//     Products of bf16 values are exact; the dot products are fp32 sums.
+//   * Epilogue per 32x32 block and lane, in registers: y = dot * (1/||k_j||)
+//     (16 multiplies), the block maximum by a 3-input max tree, then one
+//     compare and two selects keep (running max, first tile attaining it).
+//     The count needs y > tau*||k_i||; the 16 compares run only when some
+//     lane's block maximum crosses that threshold (rare: twins are sparse).
+//   * Tiles that touch the |i-j| <= w band or the ragged tail (a few per row
+//     block) skip the update in the sweep and are recomputed with masking at
+//     the end of their stage, in tile order; there an exact tie with the
+//     running maximum goes to the lower tile, as it would in column order.
 //   * Which of the 16 columns of the winning tile holds the maximum is not
 //     tracked in the sweep; after it, each lane recomputes its 16 candidates
 //     exactly in fp64 (bf16 products are exact) and keeps the largest, lowest
@@ -38,26 +51,82 @@
 
 #include "internal.h"
 
+#ifndef TWINKV_GRAM64_RB
+#define TWINKV_GRAM64_RB 4
+#endif
+#ifndef TWINKV_GRAM64_WAVES
+#define TWINKV_GRAM64_WAVES 4
+#endif
+#ifndef TWINKV_GRAM64_SC
+#define TWINKV_GRAM64_SC 128
+#endif
+#ifndef TWINKV_GRAM128_RB
+#define TWINKV_GRAM128_RB 2
+#endif
+#ifndef TWINKV_GRAM128_WAVES
+#define TWINKV_GRAM128_WAVES 4
+#endif
+#ifndef TWINKV_GRAM128_SC
+#define TWINKV_GRAM128_SC 64
+#endif
+
+#define TWINKV_LDS __attribute__((address_space(3)))
+#define TWINKV_GLOBAL __attribute__((address_space(1)))
+#define TWINKV_INLINE __attribute__((always_inline))
+
 namespace twinkv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kWaves = 4;
-constexpr int kRowBlocks = 4;  // 32-row blocks per wave
-constexpr int kStageCols = 64;
-constexpr int kTilesPerStage = kStageCols / 32;
-static_assert(kWaves * kRowBlocks * 32 == kGramRowsPerWG, "row split");
-
 template <int D>
-struct Smem {
-  uint4 keys[2][kStageCols * (D / 8)];
-  float rinv[2][kStageCols];
-  int32_t pos[2][kStageCols];
+struct Shape;
+template <>
+struct Shape<64> {
+  static constexpr int RB = TWINKV_GRAM64_RB, WAVES = TWINKV_GRAM64_WAVES, SC = TWINKV_GRAM64_SC;
+};
+template <>
+struct Shape<128> {
+  static constexpr int RB = TWINKV_GRAM128_RB, WAVES = TWINKV_GRAM128_WAVES, SC = TWINKV_GRAM128_SC;
 };
 
+template <int D>
+constexpr int rows_per_wg() {
+  return Shape<D>::WAVES * Shape<D>::RB * 32;
+}
+
+// vmcnt(0), other counters untouched (gfx9 s_waitcnt encoding)
+constexpr unsigned kWaitVm0 = 0x0F70;
+
+// One stage buffer: column keys (swizzled 16-byte chunks), inverse norms and
+// positions (repair mode).
+template <int D, int SC>
+struct Stage {
+  uint4 keys[SC * (D / 8)];
+  float rinv[SC];
+  int32_t pos[SC];
+};
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const TWINKV_GLOBAL void*)src, (TWINKV_LDS void*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const TWINKV_GLOBAL void*)src, (TWINKV_LDS void*)lds_wave_base, 4, 0, 0);
+}
+
 __device__ __forceinline__ float max3f(float a, float b, float c) { return __builtin_fmaxf(a, __builtin_fmaxf(b, c)); }
+
+__device__ __forceinline__ float max16(const float* y) {
+  const float m01 = max3f(y[0], y[1], y[2]);
+  const float m02 = max3f(y[3], y[4], y[5]);
+  const float m03 = max3f(y[6], y[7], y[8]);
+  const float m04 = max3f(y[9], y[10], y[11]);
+  const float m05 = max3f(y[12], y[13], y[14]);
+  const float m11 = max3f(m01, m02, m03);
+  const float m12 = max3f(m04, m05, y[15]);
+  return __builtin_fmaxf(m11, m12);
+}
 
 __device__ __forceinline__ double dot8_exact(uint4 a, uint4 b) {
   const uint32_t x[4] = {a.x, a.y, a.z, a.w};
@@ -75,14 +144,25 @@ __device__ __forceinline__ double dot8_exact(uint4 a, uint4 b) {
 __device__ __forceinline__ int tile_col(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
 template <int D, int MODE>
-__global__ __launch_bounds__(256, 1) void gram_kernel(GramArgs a) {
-  constexpr int CH = D / 8;       // 16-byte chunks per key row
-  constexpr int KS = D / 16;      // MFMA k-steps
-  constexpr int LOADS = kStageCols * CH / 256;
-  __shared__ Smem<D> sm;
+__global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gram_kernel(GramArgs a) {
+  constexpr int RB = Shape<D>::RB;
+  constexpr int WAVES = Shape<D>::WAVES;
+  constexpr int SC = Shape<D>::SC;
+  constexpr int NT = 64 * WAVES;   // threads
+  constexpr int ROWS = rows_per_wg<D>();
+  constexpr int CH = D / 8;        // 16-byte chunks per key row
+  constexpr int KS = D / 16;       // MFMA k-steps
+  constexpr int LOADS = SC * CH / NT;
+  constexpr int TILES = SC / 32;
+  static_assert(LOADS * NT == SC * CH, "stage load split");
+  static_assert(SC % 64 == 0 && SC / 64 <= WAVES, "stage columns: whole waves load rinv");
+  // two distinct LDS objects, so the compiler can tell the buffer being read
+  // from the one being filled
+  __shared__ Stage<D, SC> buf0;
+  __shared__ Stage<D, SC> buf1;
 
   const int64_t N = a.N;
-  const int64_t bph = (N + kGramRowsPerWG - 1) / kGramRowsPerWG;
+  const int64_t bph = (N + ROWS - 1) / ROWS;
   const int64_t total = a.G * bph;
   const int64_t per_xcd = (total + 7) / 8;
   const int64_t logical = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -92,23 +172,24 @@ __global__ __launch_bounds__(256, 1) void gram_kernel(GramArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
   const int lrow = lane & 31;
   const int w = a.window;
-  const int row0 = (int)(rb * kGramRowsPerWG) + wave * (kRowBlocks * 32);
+  const int row0 = (int)(rb * ROWS) + wave * (RB * 32);
 
   const uint4* Kg = reinterpret_cast<const uint4*>(a.keys) + (size_t)g * N * CH;
-  const float* rinv_g = a.rinv + (size_t)g * N;
-  const int32_t* pos_g = (MODE == GRAM_REPAIR) ? a.pos + (size_t)g * N : nullptr;
+  const uint4* Cg = reinterpret_cast<const uint4*>(a.col_keys) + (size_t)g * N * CH;
+  const float* crinv_g = a.col_rinv + (size_t)g * N;
+  const int32_t* cpos_g = (MODE == GRAM_REPAIR) ? a.col_pos + (size_t)g * N : nullptr;
   const int ncols = (MODE == GRAM_REPAIR) ? a.ncols[g] : (int)N;
 
   // ---- row keys as MFMA B operands, row state
-  bf16x8 brow[kRowBlocks][KS];
-  float thr[kRowBlocks], best[kRowBlocks];
-  int btile[kRowBlocks], cnt[kRowBlocks];
+  bf16x8 brow[RB][KS];
+  float thr[RB], best[RB];
+  int btile[RB], cnt[RB];
 #pragma unroll
-  for (int b = 0; b < kRowBlocks; ++b) {
+  for (int b = 0; b < RB; ++b) {
     const int i = row0 + 32 * b + lrow;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -116,147 +197,185 @@ __global__ __launch_bounds__(256, 1) void gram_kernel(GramArgs a) {
       if (i < N) v = Kg[(size_t)i * CH + 2 * s + h];
       brow[b][s] = __builtin_bit_cast(bf16x8, v);
     }
-    thr[b] = (i < N) ? (float)(a.tau * sqrt(a.nsq[(size_t)g * N + i])) : __builtin_inff();
+    thr[b] = (i < N && MODE == GRAM_SCORE) ? (float)(a.tau * sqrt(a.nsq[(size_t)g * N + i])) : __builtin_inff();
     best[b] = -__builtin_inff();
     btile[b] = -1;
     cnt[b] = 0;
   }
 
-  // ---- stage loader: global -> registers -> LDS
-  uint4 pre[LOADS];
-  float pre_r = 0.0f;
-  int32_t pre_p = INT_MAX;
-  auto fetch = [&](int64_t col0) {
+  // ---- stage issue: direct loads into one LDS buffer, all addresses valid
+  auto issue = [&](int col0, Stage<D, SC>& sb) TWINKV_INLINE {
+    const int lastc = ncols - 1;
 #pragma unroll
     for (int t = 0; t < LOADS; ++t) {
-      const int q = tid + 256 * t;
-      const int c = q / CH, k = q % CH;
-      const int64_t col = col0 + c;
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (col < ncols) {
-        const int64_t row = (MODE == GRAM_REPAIR) ? pos_g[col] : col;
-        v = Kg[(size_t)row * CH + k];
-      }
-      pre[t] = v;
+      const int q = tid + NT * t;  // LDS slot written by this lane
+      const int c = q / CH;
+      const int k = (q % CH) ^ (c & 7);
+      const int col = col0 + c < lastc ? col0 + c : lastc;
+      dma16(Cg + (size_t)col * CH + k, &sb.keys[NT * t + wave * 64]);
     }
-    if (tid < kStageCols) {
-      const int64_t col = col0 + tid;
-      pre_r = 0.0f;
-      pre_p = INT_MAX;
-      if (col < ncols) {
-        const int64_t row = (MODE == GRAM_REPAIR) ? pos_g[col] : col;
-        pre_r = rinv_g[row];
-        pre_p = (int32_t)row;
-      }
-    }
-  };
-  auto commit = [&](int buf) {
-#pragma unroll
-    for (int t = 0; t < LOADS; ++t) {
-      const int q = tid + 256 * t;
-      const int c = q / CH, k = q % CH;
-      sm.keys[buf][c * CH + (k ^ (c & 7))] = pre[t];
-    }
-    if (tid < kStageCols) {
-      sm.rinv[buf][tid] = pre_r;
-      sm.pos[buf][tid] = pre_p;
+    if (wave < SC / 64) {
+      const int col = col0 + tid < lastc ? col0 + tid : lastc;
+      dma4(crinv_g + col, &sb.rinv[wave * 64]);
+      if (MODE == GRAM_REPAIR) dma4(cpos_g + col, &sb.pos[wave * 64]);
     }
   };
 
-  const int nstages = (ncols + kStageCols - 1) / kStageCols;
-  if (nstages > 0) {
-    fetch(0);
-    commit(0);
-  }
-  __syncthreads();
-
-  for (int st = 0; st < nstages; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nstages) fetch((int64_t)(st + 1) * kStageCols);
-
+  // ---- per-tile pieces
+  auto load_a = [&](const Stage<D, SC>& sb, int tt, bf16x8 (&A)[KS]) TWINKV_INLINE {
+    const int ca = tt * 32 + lrow;  // this lane's A-operand column
 #pragma unroll
-    for (int tt = 0; tt < kTilesPerStage; ++tt) {
-      const int cb = tt * 32;  // first column of the tile inside the stage
-      const int tile = st * kTilesPerStage + tt;
-      const int c0 = tile * 32;
+    for (int s = 0; s < KS; ++s) A[s] = __builtin_bit_cast(bf16x8, sb.keys[ca * CH + ((2 * s + h) ^ (ca & 7))]);
+  };
+  auto load_rv = [&](const Stage<D, SC>& sb, int tt, float (&rv)[16]) TWINKV_INLINE {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const float4 r4 = *reinterpret_cast<const float4*>(&sb.rinv[tt * 32 + 8 * gq + 4 * h]);
+      rv[4 * gq + 0] = r4.x;
+      rv[4 * gq + 1] = r4.y;
+      rv[4 * gq + 2] = r4.z;
+      rv[4 * gq + 3] = r4.w;
+    }
+  };
+  // true when some block of tile tt touches the |i-j| <= w band or the tail
+  // (wave-uniform)
+  auto tile_masked = [&](const Stage<D, SC>& sb, int st, int tt) TWINKV_INLINE {
+    const int c0 = (st * TILES + tt) * 32;
+    int pmin, pmax;
+    if (MODE == GRAM_REPAIR) {
+      pmin = __builtin_amdgcn_readfirstlane(sb.pos[tt * 32]);
+      pmax = __builtin_amdgcn_readfirstlane(sb.pos[tt * 32 + 31]);
+    } else {
+      pmin = c0;
+      pmax = c0 + 31;
+    }
+    return (c0 + 31 >= ncols) || (pmin <= row0 + RB * 32 - 1 + w && pmax >= row0 - w);
+  };
+  // count of y > tau*||k_i|| over the 16 values of each block
+  auto count_tile = [&](const f32x16 (&y)[RB]) TWINKV_INLINE {
+    if (MODE != GRAM_SCORE) return;
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      int c = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) c += (y[b][r] > thr[b]) ? 1 : 0;
+      cnt[b] += c;
+    }
+  };
+
+  // ---- one stage of the sweep; returns the tiles (bit tt) left for the
+  // masked path
+  auto sweep = [&](int st, const Stage<D, SC>& sb) TWINKV_INLINE {
+    unsigned deferred = 0;
+#pragma unroll
+    for (int tt = 0; tt < TILES; ++tt) {
+      const int tile = st * TILES + tt;
       bf16x8 A[KS];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int c = cb + lrow;
-        const int k = 2 * s + h;
-        A[s] = __builtin_bit_cast(bf16x8, sm.keys[buf][c * CH + (k ^ (c & 7))]);
-      }
+      load_a(sb, tt, A);
       float rv[16];
+      load_rv(sb, tt, rv);
+      f32x16 y[RB];
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const float4 r4 = *reinterpret_cast<const float4*>(&sm.rinv[buf][cb + 8 * gq + 4 * h]);
-        rv[4 * gq + 0] = r4.x;
-        rv[4 * gq + 1] = r4.y;
-        rv[4 * gq + 2] = r4.z;
-        rv[4 * gq + 3] = r4.w;
+      for (int b = 0; b < RB; ++b) {
+        y[b] = (f32x16){};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) y[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], brow[b][s], y[b], 0, 0, 0);
       }
-      int pmin, pmax;
-      if (MODE == GRAM_REPAIR) {
-        pmin = __builtin_amdgcn_readfirstlane(sm.pos[buf][cb]);
-        pmax = __builtin_amdgcn_readfirstlane(sm.pos[buf][cb + 31]);
-      } else {
-        pmin = c0;
-        pmax = c0 + 31;
+      if (tile_masked(sb, st, tt)) {
+        deferred |= 1u << tt;
+        continue;
       }
-      const bool tail = (c0 + 31 >= ncols);
+      unsigned over = 0;
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        float yy[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          y[b][r] *= rv[r];
+          yy[r] = y[b][r];
+        }
+        const float m = max16(yy);
+        btile[b] = m > best[b] ? tile : btile[b];
+        best[b] = __builtin_fmaxf(best[b], m);
+        over |= (unsigned)(m > thr[b]);
+      }
+      if (__ballot(over != 0u) != 0ull) count_tile(y);
+    }
+    return deferred;
+  };
 
+  // ---- masked tile, recomputed: y = dot * rinv_j with the band and the tail
+  // excluded; one code copy, reached with the whole wave active
+  auto masked_tile = [&](const Stage<D, SC>& sb, int st, int tt) TWINKV_INLINE {
+    const int tile = st * TILES + tt;
+    const int c0 = tile * 32;
+    bf16x8 A[KS];
+    load_a(sb, tt, A);
+    float rv[16];
+    load_rv(sb, tt, rv);
+    int jpos[16];
+    bool cval[16];
 #pragma unroll
-      for (int b = 0; b < kRowBlocks; ++b) {
-        f32x16 acc = {};
+    for (int r = 0; r < 16; ++r) {
+      const int q = tile_col(r, h);
+      cval[r] = c0 + q < ncols;  // columns past the end hold clamped copies
+      jpos[r] = (MODE == GRAM_REPAIR) ? sb.pos[tt * 32 + q] : c0 + q;
+    }
+    f32x16 y[RB];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], brow[b][s], acc, 0, 0, 0);
-        float y[16];
+    for (int b = 0; b < RB; ++b) {
+      y[b] = (f32x16){};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) y[r] = acc[r] * rv[r];
-
-        const int r0 = row0 + 32 * b;
-        const bool masked = tail || (pmin <= r0 + 31 + w && pmax >= r0 - w);
-        if (masked) {
-          const int i = r0 + lrow;
+      for (int s = 0; s < KS; ++s) y[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], brow[b][s], y[b], 0, 0, 0);
+      const int i = row0 + 32 * b + lrow;
+      float yy[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int q = tile_col(r, h);
-            const int col = c0 + q;
-            const int j = (MODE == GRAM_REPAIR) ? sm.pos[buf][cb + q] : col;
-            const int dist = i > j ? i - j : j - i;
-            if (!(col < ncols && dist > w)) y[r] = -__builtin_inff();
-          }
-        }
-        const float m01 = max3f(y[0], y[1], y[2]);
-        const float m02 = max3f(y[3], y[4], y[5]);
-        const float m03 = max3f(y[6], y[7], y[8]);
-        const float m04 = max3f(y[9], y[10], y[11]);
-        const float m05 = max3f(y[12], y[13], y[14]);
-        const float m11 = max3f(m01, m02, m03);
-        const float m12 = max3f(m04, m05, y[15]);
-        const float m = __builtin_fmaxf(m11, m12);
-        if (m > best[b]) {
-          best[b] = m;
-          btile[b] = tile;
-        }
-        if (MODE == GRAM_SCORE) {
-          if (m > thr[b]) {
-            int c = 0;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) c += (y[r] > thr[b]) ? 1 : 0;
-            cnt[b] += c;
-          }
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int dist = i > jpos[r] ? i - jpos[r] : jpos[r] - i;
+        y[b][r] = (cval[r] && dist > w) ? y[b][r] * rv[r] : -__builtin_inff();
+        yy[r] = y[b][r];
+      }
+      const float m = max16(yy);
+      // processed after later tiles of the stage: an equal value from an
+      // earlier tile takes over, as it would have in column order
+      if (m > best[b] || (m == best[b] && tile < btile[b])) {
+        best[b] = m;
+        btile[b] = tile;
       }
     }
+    count_tile(y);
+  };
 
-    if (st + 1 < nstages) commit(buf ^ 1);
-    __syncthreads();
+  const int nstages = (ncols + SC - 1) / SC;
+  if (nstages > 0) issue(0, buf0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+#pragma unroll 1
+  for (int st = 0; st < nstages; ++st) {
+    unsigned deferred;
+    if ((st & 1) == 0) {
+      if (st + 1 < nstages) issue((st + 1) * SC, buf1);
+      deferred = sweep(st, buf0);
+    } else {
+      if (st + 1 < nstages) issue((st + 1) * SC, buf0);
+      deferred = sweep(st, buf1);
+    }
+    deferred = __builtin_amdgcn_readfirstlane(deferred);
+    const Stage<D, SC>* cur = (st & 1) ? &buf1 : &buf0;
+#pragma unroll 1
+    while (deferred != 0u) {
+      const int tt = __builtin_ctz(deferred);
+      deferred &= deferred - 1u;
+      masked_tile(*cur, st, tt);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();  // next buffer complete for every wave; this one free
   }
 
   // ---- exact fp64 fixup of the best twin, merge of half-waves, outputs
-#pragma unroll 1
-  for (int b = 0; b < kRowBlocks; ++b) {
+  // (unrolled: the per-block state stays in registers)
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
     const int i = row0 + 32 * b + lrow;
     const bool row_ok = i < N;
     double bb = -1.0;
@@ -264,11 +383,11 @@ __global__ __launch_bounds__(256, 1) void gram_kernel(GramArgs a) {
     if (row_ok && btile[b] >= 0) {
       const double ni = a.nsq[(size_t)g * N + i];
       const uint4* ki = Kg + (size_t)i * CH;
-#pragma unroll 1
+#pragma unroll 4
       for (int r = 0; r < 16; ++r) {
         const int col = btile[b] * 32 + tile_col(r, h);
         if (col >= ncols) continue;
-        const int j = (MODE == GRAM_REPAIR) ? pos_g[col] : col;
+        const int j = (MODE == GRAM_REPAIR) ? cpos_g[col] : col;
         const int dist = i > j ? i - j : j - i;
         if (dist <= w) continue;
         const uint4* kj = Kg + (size_t)j * CH;
@@ -314,11 +433,12 @@ __global__ __launch_bounds__(256, 1) void gram_kernel(GramArgs a) {
 
 template <int D, int MODE>
 hipError_t launch_dm(const GramArgs& a, hipStream_t stream) {
-  const int64_t bph = (a.N + kGramRowsPerWG - 1) / kGramRowsPerWG;
+  constexpr int ROWS = rows_per_wg<D>();
+  const int64_t bph = (a.N + ROWS - 1) / ROWS;
   const int64_t total = a.G * bph;
   const int64_t grid = 8 * ((total + 7) / 8);
   if (grid > INT_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gram_kernel<D, MODE>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((gram_kernel<D, MODE>), dim3((unsigned)grid), dim3(64 * Shape<D>::WAVES), 0, stream, a);
   return hipGetLastError();
 }
 

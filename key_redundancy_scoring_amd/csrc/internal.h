@@ -10,15 +10,13 @@ namespace twinkv {
 // Column source for the Gram sweep.
 enum GramMode { GRAM_SCORE = 0, GRAM_REPAIR = 1 };
 
-// Rows of one head handled by one workgroup of the Gram kernel.
-constexpr int kGramRowsPerWG = 512;
-
 struct GramArgs {
-  const uint16_t* keys;   // bf16 [G][N][d]
-  const float* rinv;      // 1/||k|| in fp32 [G][N] (0 for a zero key)
-  const double* nsq;      // ||k||^2 in fp64 [G][N]
-  const int32_t* pos;     // repair: retained positions of each head, ascending [G][N]
-  const int32_t* ncols;   // repair: number of retained positions per head [G]
+  const uint16_t* keys;      // bf16 [G][N][d]: the rows (and the fp64 fixup's operands)
+  const double* nsq;         // ||k||^2 in fp64 [G][N]
+  const uint16_t* col_keys;  // bf16 [G][N][d]: the streamed columns (score: keys; repair: S0 compacted)
+  const float* col_rinv;     // 1/||k|| in fp32 of each column [G][N] (0 for a zero key)
+  const int32_t* col_pos;    // repair: original position of each compacted column, ascending [G][N]
+  const int32_t* ncols;      // repair: number of retained positions per head [G]
   const double* energy;   // score: ||v||^2 [G][N]
   int64_t G, N;
   int32_t d, window;
@@ -31,9 +29,12 @@ struct GramArgs {
   double* omega;          // score only, may be null
 };
 
+// nsq = ||k||^2 (fp64), rinv = 1/||k|| (fp32, 0 for a zero key) and energy =
+// ||v||^2 (fp64; skipped when values is null).
 hipError_t launch_norms(const uint16_t* keys, const uint16_t* values, int64_t nkeys, int d, double* nsq,
                         float* rinv, double* energy, hipStream_t stream);
 hipError_t launch_gram(const GramArgs& a, int mode, hipStream_t stream);
+
 
 struct SelectArgs {
   const double* score;
@@ -49,6 +50,9 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 
 hipError_t launch_compact(const uint8_t* keep_in, int64_t G, int64_t N, int32_t* pos, int32_t* ncols,
                           hipStream_t stream);
+// Copy the retained keys and their inverse norms into column order.
+hipError_t launch_gather(const uint16_t* keys, const float* rinv, const int32_t* pos, const int32_t* ncols, int64_t G,
+                         int64_t N, int d, uint16_t* ckeys, float* crinv, hipStream_t stream);
 
 struct SwapArgs {
   const uint8_t* keep_in;

@@ -17,6 +17,8 @@
 //   m-th key; the m chosen members of each side are gathered in position
 //   order and put in rank order by a stable LSD radix sort, which keeps equal
 //   keys in position order.
+#include <limits.h>
+
 #include "blockops.h"
 
 namespace twinkv {
@@ -38,6 +40,35 @@ __global__ __launch_bounds__(kBT) void compact_kernel(const uint8_t* __restrict_
     base += tot;
   }
   if (threadIdx.x == 0) ncols[g] = base;
+}
+
+// Copy retained key rows (and their inverse norms) into column order, so the
+// restricted Gram sweep streams contiguous rows: ckeys[g][k] = keys[g][pos[g][k]]
+// for k < ncols[g].  One 16-byte chunk per thread and step.
+template <int D>
+__global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ keys, const float* __restrict__ rinv,
+                                                     const int32_t* __restrict__ pos,
+                                                     const int32_t* __restrict__ ncols, int64_t N, int64_t bph,
+                                                     uint4* __restrict__ ckeys, float* __restrict__ crinv) {
+  constexpr int CH = D / 8;
+  constexpr int STEPS = 4;
+  const int64_t g = blockIdx.x / bph;
+  const int64_t bx = blockIdx.x % bph;
+  const int64_t lim = (int64_t)ncols[g] * CH;
+  const int32_t* pg = pos + g * N;
+  const uint4* kg = keys + g * N * CH;
+  uint4* cg = ckeys + g * N * CH;
+#pragma unroll
+  for (int t = 0; t < STEPS; ++t) {
+    const int64_t q = (bx * STEPS + t) * 256 + threadIdx.x;
+    if (q < lim) {
+      const int64_t k = q / CH;
+      const int c = (int)(q % CH);
+      const int64_t src = pg[k];
+      cg[q] = kg[src * CH + c];
+      if (c == 0) crinv[g * N + k] = rinv[g * N + src];
+    }
+  }
 }
 
 // Gather the top-m members of one side, in position order, into (lk, li).
@@ -140,6 +171,21 @@ __global__ __launch_bounds__(kBT) void swap_kernel(SwapArgs a) {
 hipError_t launch_compact(const uint8_t* keep_in, int64_t G, int64_t N, int32_t* pos, int32_t* ncols,
                           hipStream_t stream) {
   hipLaunchKernelGGL(compact_kernel, dim3((unsigned)G), dim3(kBT), 0, stream, keep_in, N, pos, ncols);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const uint16_t* keys, const float* rinv, const int32_t* pos, const int32_t* ncols, int64_t G,
+                         int64_t N, int d, uint16_t* ckeys, float* crinv, hipStream_t stream) {
+  const int64_t chunks = N * (d / 8);
+  const int64_t bph = (chunks + 1023) / 1024;
+  if (bph * G > INT_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(bph * G));
+  if (d == 64)
+    hipLaunchKernelGGL((gather_kernel<64>), grid, dim3(256), 0, stream, (const uint4*)keys, rinv, pos, ncols, N, bph,
+                       (uint4*)ckeys, crinv);
+  else
+    hipLaunchKernelGGL((gather_kernel<128>), grid, dim3(256), 0, stream, (const uint4*)keys, rinv, pos, ncols, N, bph,
+                       (uint4*)ckeys, crinv);
   return hipGetLastError();
 }
 
