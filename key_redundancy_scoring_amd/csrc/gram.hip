@@ -23,7 +23,7 @@
 //     repair mode.  Each lane of a direct load writes 16 bytes at
 //     base + 16*lane, so the XOR swizzle that spreads the MFMA A-operand reads
 //     over the LDS banks (16-byte chunk k of column c sits at slot
-//     c*CH + (k ^ (c & 7))) is applied by choosing which global chunk each
+//     c*CH + (k ^ swz(c))) is applied by choosing which global chunk each
 //     lane fetches.  Columns past the end are clamped to the last one; the
 //     tiles that hold them are handled by the masked path below.
 //   * v_mfma_f32_32x32x16_bf16 with A = 32 column keys, B = 32 row keys gives
@@ -36,14 +36,17 @@
 //     The count needs y > tau*||k_i||; the 16 compares run only when some
 //     lane's block maximum crosses that threshold (rare: twins are sparse).
 //   * Tiles that touch the |i-j| <= w band or the ragged tail (a few per row
-//     block) skip the update in the sweep and are recomputed with masking at
-//     the end of their stage, in tile order; there an exact tie with the
-//     running maximum goes to the lower tile, as it would in column order.
+//     block) leave the state unchanged in the sweep (branch-free: their
+//     maximum is taken as -inf) and are recomputed with masking at the end of
+//     their stage, in tile order; there an exact tie with the running maximum
+//     goes to the lower tile, as it would in column order.
 //   * Which of the 16 columns of the winning tile holds the maximum is not
-//     tracked in the sweep; after it, each lane recomputes its 16 candidates
-//     exactly in fp64 (bf16 products are exact) and keeps the largest, lowest
-//     position on ties; the two half-waves that share a row then merge.  This
-//     also makes b_i the exact fp64 cosine dot/sqrt(n_i*n_j) of the chosen pair.
+//     tracked in the sweep; after it, a lane whose half-row maximum can be the
+//     row's screens its 16 candidates in fp32 and recomputes the near-maximal
+//     ones exactly in fp64 (bf16 products are exact), keeping the largest,
+//     lowest position on ties; the two half-waves that share a row then
+//     merge.  This also makes b_i the exact fp64 cosine dot/sqrt(n_i*n_j) of
+//     the chosen pair.
 //   * Workgroup ids are remapped so each XCD (ids are dealt round-robin over
 //     8 XCDs) receives a contiguous run of row blocks: the blocks of one head
 //     sweep its key stream together out of one L2.
@@ -58,7 +61,7 @@
 #define TWINKV_GRAM64_WAVES 4
 #endif
 #ifndef TWINKV_GRAM64_SC
-#define TWINKV_GRAM64_SC 128
+#define TWINKV_GRAM64_SC 256
 #endif
 #ifndef TWINKV_GRAM128_RB
 #define TWINKV_GRAM128_RB 2
@@ -67,7 +70,7 @@
 #define TWINKV_GRAM128_WAVES 4
 #endif
 #ifndef TWINKV_GRAM128_SC
-#define TWINKV_GRAM128_SC 64
+#define TWINKV_GRAM128_SC 128
 #endif
 
 #define TWINKV_LDS __attribute__((address_space(3)))
@@ -78,6 +81,7 @@ namespace twinkv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <int D>
@@ -140,6 +144,16 @@ __device__ __forceinline__ double dot8_exact(uint4 a, uint4 b) {
   return s;
 }
 
+// XOR swizzle of the 16-byte chunks of stage column c (CH chunks per key).
+// Chunk k of column c lives at slot c*CH + (k ^ swz(c)).  For the A-operand
+// reads (lane l reads chunk k of column l mod 32) this puts any 8 consecutive
+// lanes on distinct 16-byte bank groups of a 128-byte row and any 16 on
+// distinct groups of a 256-byte row.
+template <int CH>
+__device__ __forceinline__ int swz(int c) {
+  return CH == 8 ? ((c ^ (c >> 3)) & 7) : (c & 15);
+}
+
 // column offset (within a 32-column tile) of accumulator r in half-wave h
 __device__ __forceinline__ int tile_col(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
@@ -156,8 +170,8 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
   constexpr int TILES = SC / 32;
   static_assert(LOADS * NT == SC * CH, "stage load split");
   static_assert(SC % 64 == 0 && SC / 64 <= WAVES, "stage columns: whole waves load rinv");
-  // two distinct LDS objects, so the compiler can tell the buffer being read
-  // from the one being filled
+  // distinct LDS objects, so the compiler can tell the buffer being read
+  // from the ones being filled
   __shared__ Stage<D, SC> buf0;
   __shared__ Stage<D, SC> buf1;
 
@@ -210,7 +224,7 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
     for (int t = 0; t < LOADS; ++t) {
       const int q = tid + NT * t;  // LDS slot written by this lane
       const int c = q / CH;
-      const int k = (q % CH) ^ (c & 7);
+      const int k = (q % CH) ^ swz<CH>(c);
       const int col = col0 + c < lastc ? col0 + c : lastc;
       dma16(Cg + (size_t)col * CH + k, &sb.keys[NT * t + wave * 64]);
     }
@@ -225,7 +239,7 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
   auto load_a = [&](const Stage<D, SC>& sb, int tt, bf16x8 (&A)[KS]) TWINKV_INLINE {
     const int ca = tt * 32 + lrow;  // this lane's A-operand column
 #pragma unroll
-    for (int s = 0; s < KS; ++s) A[s] = __builtin_bit_cast(bf16x8, sb.keys[ca * CH + ((2 * s + h) ^ (ca & 7))]);
+    for (int s = 0; s < KS; ++s) A[s] = __builtin_bit_cast(bf16x8, sb.keys[ca * CH + ((2 * s + h) ^ swz<CH>(ca))]);
   };
   auto load_rv = [&](const Stage<D, SC>& sb, int tt, float (&rv)[16]) TWINKV_INLINE {
 #pragma unroll
@@ -237,163 +251,254 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
       rv[4 * gq + 3] = r4.w;
     }
   };
-  // true when some block of tile tt touches the |i-j| <= w band or the tail
-  // (wave-uniform)
-  auto tile_masked = [&](const Stage<D, SC>& sb, int st, int tt) TWINKV_INLINE {
-    const int c0 = (st * TILES + tt) * 32;
-    int pmin, pmax;
-    if (MODE == GRAM_REPAIR) {
-      pmin = __builtin_amdgcn_readfirstlane(sb.pos[tt * 32]);
-      pmax = __builtin_amdgcn_readfirstlane(sb.pos[tt * 32 + 31]);
-    } else {
-      pmin = c0;
-      pmax = c0 + 31;
-    }
-    return (c0 + 31 >= ncols) || (pmin <= row0 + RB * 32 - 1 + w && pmax >= row0 - w);
-  };
-  // count of y > tau*||k_i|| over the 16 values of each block
-  auto count_tile = [&](const f32x16 (&y)[RB]) TWINKV_INLINE {
-    if (MODE != GRAM_SCORE) return;
-#pragma unroll
-    for (int b = 0; b < RB; ++b) {
-      int c = 0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) c += (y[b][r] > thr[b]) ? 1 : 0;
-      cnt[b] += c;
-    }
-  };
-
-  // ---- one stage of the sweep; returns the tiles (bit tt) left for the
-  // masked path
-  auto sweep = [&](int st, const Stage<D, SC>& sb) TWINKV_INLINE {
-    unsigned deferred = 0;
+  // Bit tt set: some block of the wave's rows meets the |i-j| <= w band or
+  // the ragged tail in tile tt of stage st (wave-uniform).
+  auto masked_tiles = [&](const Stage<D, SC>& sb, int st) TWINKV_INLINE {
+    unsigned bits = 0;
 #pragma unroll
     for (int tt = 0; tt < TILES; ++tt) {
-      const int tile = st * TILES + tt;
-      bf16x8 A[KS];
-      load_a(sb, tt, A);
-      float rv[16];
-      load_rv(sb, tt, rv);
-      f32x16 y[RB];
-#pragma unroll
-      for (int b = 0; b < RB; ++b) {
-        y[b] = (f32x16){};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) y[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], brow[b][s], y[b], 0, 0, 0);
+      const int c0 = (st * TILES + tt) * 32;
+      int pmin, pmax;
+      if (MODE == GRAM_REPAIR) {
+        pmin = __builtin_amdgcn_readfirstlane(sb.pos[tt * 32]);
+        pmax = __builtin_amdgcn_readfirstlane(sb.pos[tt * 32 + 31]);
+      } else {
+        pmin = c0;
+        pmax = c0 + 31;
       }
-      if (tile_masked(sb, st, tt)) {
-        deferred |= 1u << tt;
-        continue;
-      }
-      unsigned over = 0;
-#pragma unroll
-      for (int b = 0; b < RB; ++b) {
-        float yy[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          y[b][r] *= rv[r];
-          yy[r] = y[b][r];
-        }
-        const float m = max16(yy);
-        btile[b] = m > best[b] ? tile : btile[b];
-        best[b] = __builtin_fmaxf(best[b], m);
-        over |= (unsigned)(m > thr[b]);
-      }
-      if (__ballot(over != 0u) != 0ull) count_tile(y);
+      const bool mk = (c0 + 31 >= ncols) || (pmin <= row0 + RB * 32 - 1 + w && pmax >= row0 - w);
+      bits |= (unsigned)mk << tt;
     }
-    return deferred;
+    return bits;
   };
-
-  // ---- masked tile, recomputed: y = dot * rinv_j with the band and the tail
-  // excluded; one code copy, reached with the whole wave active
-  auto masked_tile = [&](const Stage<D, SC>& sb, int st, int tt) TWINKV_INLINE {
-    const int tile = st * TILES + tt;
-    const int c0 = tile * 32;
-    bf16x8 A[KS];
-    load_a(sb, tt, A);
-    float rv[16];
-    load_rv(sb, tt, rv);
-    int jpos[16];
-    bool cval[16];
+  // Bit tt set: tile tt of stage st reaches past the last column.
+  auto tail_tiles = [&](int st) TWINKV_INLINE {
+    unsigned bits = 0;
+#pragma unroll
+    for (int tt = 0; tt < TILES; ++tt) bits |= (unsigned)((st * TILES + tt) * 32 + 31 >= ncols) << tt;
+    return bits;
+  };
+  // count of y > tau*||k_i|| over the 16 values of a block
+  auto count16 = [&](const f32x16& y, int b) TWINKV_INLINE {
+    int c = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c += (y[r] > thr[b]) ? 1 : 0;
+    cnt[b] += c;
+  };
+  auto mfma_block = [&](const bf16x8 (&A)[KS], int b, f32x16& acc) TWINKV_INLINE {
+    acc = (f32x16){};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], brow[b][s], acc, 0, 0, 0);
+  };
+  // Epilogue of block b of a tile whose dots are in acc: y = dot * rinv_j, the
+  // block maximum (neutralised to -inf on a masked tile by neg), running
+  // maximum and first tile, count when some lane crosses tau*||k_i||.
+  auto epilogue = [&](f32x16& acc, int b, const float (&rv)[16], float neg, int tile) TWINKV_INLINE {
+    float yy[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int q = tile_col(r, h);
-      cval[r] = c0 + q < ncols;  // columns past the end hold clamped copies
-      jpos[r] = (MODE == GRAM_REPAIR) ? sb.pos[tt * 32 + q] : c0 + q;
+      acc[r] *= rv[r];
+      yy[r] = acc[r];
     }
-    f32x16 y[RB];
-#pragma unroll
-    for (int b = 0; b < RB; ++b) {
-      y[b] = (f32x16){};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) y[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], brow[b][s], y[b], 0, 0, 0);
-      const int i = row0 + 32 * b + lrow;
-      float yy[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int dist = i > jpos[r] ? i - jpos[r] : jpos[r] - i;
-        y[b][r] = (cval[r] && dist > w) ? y[b][r] * rv[r] : -__builtin_inff();
-        yy[r] = y[b][r];
-      }
-      const float m = max16(yy);
-      // processed after later tiles of the stage: an equal value from an
-      // earlier tile takes over, as it would have in column order
-      if (m > best[b] || (m == best[b] && tile < btile[b])) {
-        best[b] = m;
-        btile[b] = tile;
-      }
+    const float m = __builtin_fminf(max16(yy), neg);
+    btile[b] = m > best[b] ? tile : btile[b];
+    best[b] = __builtin_fmaxf(best[b], m);
+    if (MODE == GRAM_SCORE) {
+      if (__ballot(m > thr[b]) != 0ull) count16(acc, b);
     }
-    count_tile(y);
+  };
+  // Keep the next tile's MFMAs between the epilogue's vector instructions.
+  auto interleave = [&]() TWINKV_INLINE {
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // up to seven VALU
+    }
   };
 
+  // ---- the sweep: a rolling pipeline over (tile, block).  After block b's
+  // epilogue for tile t its accumulator takes the MFMAs of block b for tile
+  // t+1, which run while block b+1's epilogue executes.  The epilogue reads
+  // only registers, so once the last tile's operands of stage s are read the
+  // one wait and barrier of the stage publish stage s+1, the loads of stage
+  // s+2 go into stage s's buffer, and the last tile's epilogue overlaps the
+  // next stage's first MFMAs.  Masked tiles only leave the state unchanged
+  // here; the band tiles are contiguous, their range is recorded.
   const int nstages = (ncols + SC - 1) / SC;
+  f32x16 acc[RB];
+  bf16x8 A[KS];
+  float rv[16], rv_next[16];
+  int band_lo = INT_MAX, band_hi = -1;  // masked tiles other than the tail
   if (nstages > 0) issue(0, buf0);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
-#pragma unroll 1
-  for (int st = 0; st < nstages; ++st) {
-    unsigned deferred;
-    if ((st & 1) == 0) {
-      if (st + 1 < nstages) issue((st + 1) * SC, buf1);
-      deferred = sweep(st, buf0);
-    } else {
-      if (st + 1 < nstages) issue((st + 1) * SC, buf0);
-      deferred = sweep(st, buf1);
+  if (nstages > 1) issue(SC, buf1);
+  if (nstages > 0) {
+    load_a(buf0, 0, A);
+#pragma unroll
+    for (int b = 0; b < RB; ++b) mfma_block(A, b, acc[b]);
+    load_rv(buf0, 0, rv);
+  }
+  auto stage = [&](int st, Stage<D, SC>& cur, const Stage<D, SC>& nxt) TWINKV_INLINE {
+    const unsigned mbits = __builtin_amdgcn_readfirstlane(masked_tiles(cur, st));
+    const unsigned tailbits = __builtin_amdgcn_readfirstlane(tail_tiles(st));
+    const unsigned bbits = mbits & ~tailbits;
+    if (bbits != 0u) {
+      band_lo = min(band_lo, st * TILES + __builtin_ctz(bbits));
+      band_hi = max(band_hi, st * TILES + 31 - __builtin_clz(bbits));
     }
-    deferred = __builtin_amdgcn_readfirstlane(deferred);
-    const Stage<D, SC>* cur = (st & 1) ? &buf1 : &buf0;
 #pragma unroll 1
-    while (deferred != 0u) {
-      const int tt = __builtin_ctz(deferred);
-      deferred &= deferred - 1u;
-      masked_tile(*cur, st, tt);
+    for (int tt = 0; tt < TILES - 1; ++tt) {
+      const int tile = st * TILES + tt;
+      load_a(cur, tt + 1, A);
+      load_rv(cur, tt + 1, rv_next);
+      const float neg = ((mbits >> tt) & 1u) ? -__builtin_inff() : __builtin_inff();
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        epilogue(acc[b], b, rv, neg, tile);
+        mfma_block(A, b, acc[b]);
+        interleave();
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rv[r] = rv_next[r];
     }
+    // every operand of this stage has been read: publish the next one
+    const bool more = st + 1 < nstages;
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();  // next buffer complete for every wave; this one free
+    __syncthreads();
+    if (st + 2 < nstages) issue((st + 2) * SC, cur);
+    if (more) {
+      load_a(nxt, 0, A);
+      load_rv(nxt, 0, rv_next);
+    }
+    const int tile = st * TILES + TILES - 1;
+    const float neg = ((mbits >> (TILES - 1)) & 1u) ? -__builtin_inff() : __builtin_inff();
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      epilogue(acc[b], b, rv, neg, tile);
+      if (more) mfma_block(A, b, acc[b]);
+      interleave();
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rv[r] = rv_next[r];
+  };
+#pragma unroll 1
+  for (int st = 0; st < nstages; st += 2) {
+    stage(st, buf0, buf1);
+    if (st + 1 >= nstages) break;
+    stage(st + 1, buf1, buf0);
+  }
+
+  // ---- masked tiles (the band range and the partial last tile), recomputed
+  // from global memory with the band and the tail excluded.  They come after
+  // later tiles: an exact tie with the running maximum goes to the lower
+  // tile, as it would have in column order.  The whole wave is active (the
+  // MFMA reads every lane).
+  {
+    const int ntiles = (ncols + 31) / 32;
+    const int last = ntiles - 1;
+    const int nband = band_hi >= 0 ? band_hi - band_lo + 1 : 0;
+    const bool last_extra = ntiles > 0 && (ncols & 31) != 0 && !(nband > 0 && last >= band_lo && last <= band_hi);
+    const int nproc = nband + (last_extra ? 1 : 0);
+#pragma unroll 1
+    for (int k = 0; k < nproc; ++k) {
+      const int t = k < nband ? band_lo + k : last;
+      const int c0 = t * 32;
+      bf16x8 Am[KS];
+      {
+        const int c = c0 + lrow < ncols ? c0 + lrow : ncols - 1;  // clamped; masked below
+#pragma unroll
+        for (int s = 0; s < KS; ++s) Am[s] = __builtin_bit_cast(bf16x8, Cg[(size_t)c * CH + 2 * s + h]);
+      }
+      float rvm[16];
+      int jpos[16];
+      bool cval[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int col = c0 + tile_col(r, h);
+        cval[r] = col < ncols;
+        const int cc = cval[r] ? col : ncols - 1;
+        rvm[r] = crinv_g[cc];
+        jpos[r] = (MODE == GRAM_REPAIR) ? cpos_g[cc] : col;
+      }
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        f32x16 y;
+        mfma_block(Am, b, y);
+        const int i = row0 + 32 * b + lrow;
+        float yy[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int dist = i > jpos[r] ? i - jpos[r] : jpos[r] - i;
+          y[r] = (cval[r] && dist > w) ? y[r] * rvm[r] : -__builtin_inff();
+          yy[r] = y[r];
+        }
+        const float m = max16(yy);
+        if (m > best[b] || (m == best[b] && t < btile[b])) {
+          best[b] = m;
+          btile[b] = t;
+        }
+        if (MODE == GRAM_SCORE) count16(y, b);
+      }
+    }
   }
 
   // ---- exact fp64 fixup of the best twin, merge of half-waves, outputs
-  // (unrolled: the per-block state stays in registers)
+  // (unrolled: the per-block state stays in registers).  Each half-wave
+  // holds, for its row, the fp32 maximum over its 16 columns of every tile
+  // and the first tile attaining it.  Only a half whose maximum can be the
+  // row's looks at its candidates; it screens the 16 candidates with fp32
+  // dot products (v_dot2 of bf16 pairs) and evaluates exactly in fp64 only
+  // those within a safe margin of the largest, which always include the
+  // exact maximum.
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     const int i = row0 + 32 * b + lrow;
     const bool row_ok = i < N;
     double bb = -1.0;
     int aa = -1;
-    if (row_ok && btile[b] >= 0) {
-      const double ni = a.nsq[(size_t)g * N + i];
+    const double ni = row_ok ? a.nsq[(size_t)g * N + i] : 0.0;
+    // |fp32 value - exact| stays below 1e-5 * ||k_i|| for the sweep's and
+    // this screen's sums of at most 128 exact products (then scaled by
+    // rinv_j); the margin is eight times that
+    const float margin = 8e-5f * (float)sqrt(ni) + 1e-30f;
+    const float other = __shfl_xor(best[b], 32);
+    const bool look = row_ok && btile[b] >= 0 && best[b] >= other - margin;
+    if (look) {
       const uint4* ki = Kg + (size_t)i * CH;
+      uint4 kr[CH];
+#pragma unroll
+      for (int k = 0; k < CH; ++k) kr[k] = ki[k];
+      float ya[16];
+      float ymax = -__builtin_inff();
 #pragma unroll 4
       for (int r = 0; r < 16; ++r) {
         const int col = btile[b] * 32 + tile_col(r, h);
-        if (col >= ncols) continue;
-        const int j = (MODE == GRAM_REPAIR) ? cpos_g[col] : col;
+        const int cc = col < ncols ? col : ncols - 1;
+        const int j = (MODE == GRAM_REPAIR) ? cpos_g[cc] : cc;
         const int dist = i > j ? i - j : j - i;
-        if (dist <= w) continue;
+        const uint4* kj = Kg + (size_t)j * CH;
+        float dotf = 0.0f;
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+          const uint4 q = kj[k];
+          dotf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[k].x), __builtin_bit_cast(bf16x2, q.x), dotf, false);
+          dotf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[k].y), __builtin_bit_cast(bf16x2, q.y), dotf, false);
+          dotf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[k].z), __builtin_bit_cast(bf16x2, q.z), dotf, false);
+          dotf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[k].w), __builtin_bit_cast(bf16x2, q.w), dotf, false);
+        }
+        ya[r] = (col < ncols && dist > w) ? dotf * crinv_g[cc] : -__builtin_inff();
+        ymax = __builtin_fmaxf(ymax, ya[r]);
+      }
+#pragma unroll 1
+      for (int r = 0; r < 16; ++r) {
+        if (!(ya[r] > -__builtin_inff() && ya[r] >= ymax - margin)) continue;  // invalid ones are -inf
+        const int col = btile[b] * 32 + tile_col(r, h);
+        const int j = (MODE == GRAM_REPAIR) ? cpos_g[col] : col;
         const uint4* kj = Kg + (size_t)j * CH;
         double dot = 0.0;
 #pragma unroll
-        for (int k = 0; k < CH; ++k) dot += dot8_exact(ki[k], kj[k]);
+        for (int k = 0; k < CH; ++k) dot += dot8_exact(kr[k], kj[k]);
         const double nn = ni * a.nsq[(size_t)g * N + j];
         double sim = nn > 0.0 ? dot / sqrt(nn) : 0.0;
         sim += 0.0;
