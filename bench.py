@@ -1,25 +1,32 @@
 """Benchmark of the key-redundancy hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+    python bench.py --calibrate-copy        # plain device copy, for counter calibration
 
 One step = one pass of the whole path over one batch of synthetic heads that
 is already resident in HBM: score (norms/energy pass + fused Gram sweep with
 the fp64 best-twin fixup and the discounted score) -> exact-budget select ->
-repair of the selected set (restricted Gram over the retained columns,
-orphan/donor ranking and swap).  The default workload is the Llama-3.2-1B
-shape: 16 layers x 8 KV heads = 128 heads, N = 32768, head dim 64, 10%
-planted near-duplicates, tau 0.9, window 64, 4 sinks, 64 recent, 50% removal.
+repair of the selected set (compaction of the retained keys, restricted Gram
+over them, orphan/donor ranking and swap).  The default workload is the
+Llama-3.2-1B shape: 16 layers x 8 KV heads = 128 heads, N = 32768, head dim
+64, 10% planted near-duplicates, tau 0.9, window 64, 4 sinks, 64 recent, 50%
+removal.
 
 Prints one JSON line.  `value` is keys (head positions) through the whole path
 per second.  `roofline` is for the dominant kernel, the score-mode Gram
-sweep, timed with HIP events recorded by the library around its launch on
+sweep, timed with HIP events that the library records around its launch on
 the stream it runs on; its `achieved` counts the algorithmic work, one
-d-length dot product (2d flop) per unordered nonlocal pair.  `cpu_baseline`
-times the fp64 oracle on a bounded sample of the same workload on the host.
+d-length dot product (2d flop) per unordered nonlocal pair, while `gram`
+also gives the dense-equivalent rate (both orders of every pair, the work the
+sweep executes).  `traffic` is the HBM traffic per launch measured with
+rocprofv3 counters for the current Gram source (null when the source has
+changed since).  `cpu_baseline` times the fp64 oracle's score stage on the
+host over row blocks of the same workload, for about 12 s.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +41,27 @@ if ROOT not in sys.path:
 METRIC = "keys scored/sec + Gram TFLOP/s (MFMA % of peak) at N=32k, 1 MI355X"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU (published: 2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0
+GRAM_SOURCE = os.path.join(ROOT, "key_redundancy_scoring_amd", "csrc", "gram.hip")
+
+# HBM traffic of one score-mode Gram launch on the default workload, from
+# rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the counters'
+# reading for a plain device copy of known size; keyed by the sha256 of the
+# Gram source the counters were taken on.
+MEASURED_TRAFFIC: dict = {
+    "755c4e4d0f073bb4390c32e5e3b3b74e013565d4c8a9ba706381188423d08a4f": {
+        "workload": (128, 32768, 64),
+        # FETCH_SIZE 2013097.75 KiB x 1.99994 (a 1 GiB copy reads 524304 KiB),
+        # WRITE_SIZE 196608 KiB x 1.0 (the same copy writes 1048576 KiB)
+        "fetch_bytes": 4122700933,
+        "write_bytes": 201326592,
+        "bytes_per_launch": 4324027525,
+    },
+}
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def algorithmic_gram_flops(N: int, d: int, window: int, G: int) -> float:
@@ -47,21 +75,48 @@ def restricted_gram_flops(N: int, K: int, d: int, G: int) -> float:
     return float(G) * N * K * 2.0 * d
 
 
-def cpu_baseline(cfg, rows: int, seed_head: int = 0):
+def cpu_baseline(cfg, seconds: float, block: int = 2048):
+    """The oracle's score stage (count, best nonlocal twin, value energy and
+    score), each row against all N positions of its head, over consecutive
+    row blocks of heads 0, 1, ... until about `seconds` of host time are
+    spent; timed on the host.  Per key this is less work than the GPU step,
+    which also selects and repairs."""
     from threadpoolctl import threadpool_info
 
     from oracle import twinkv_oracle as O
     from synth import make_head
 
-    h = make_head(cfg, seed_head)
-    sel = np.arange(rows)
-    t0 = time.perf_counter()
-    O.score_head(h["K"], h["V"], cfg.tau, cfg.window, rows=sel)
-    dt = time.perf_counter() - t0
+    done, spent, g = 0, 0.0, 0
+    while spent < seconds and g < cfg.G:
+        h = make_head(cfg, g)
+        for r0 in range(0, cfg.N, block):
+            rows = np.arange(r0, min(cfg.N, r0 + block))
+            t0 = time.perf_counter()
+            O.score_head(h["K"], h["V"], cfg.tau, cfg.window, rows=rows)
+            spent += time.perf_counter() - t0
+            done += rows.size
+            if spent >= seconds:
+                break
+        g += 1
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": rows / dt, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"score (count, best twin, energy, score) of rows 0..{rows - 1} of head {seed_head} "
-                      f"(each row against all N={cfg.N} positions), fp64 numpy/BLAS, {dt:.1f} s"}
+    return {"value": done / spent, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"score stage (count, best twin, energy, score) of the first {done} rows of heads "
+                      f"0..{g - 1} in blocks of {block}, each row against all N={cfg.N} positions of its head, "
+                      f"fp64 numpy/BLAS, {spent:.1f} s"}
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of 1 GiB, five times, for scaling the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n}), flush=True)
 
 
 def main():
@@ -71,28 +126,31 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--heads", type=int, default=None, help="override the head count (default: the workload's)")
+    ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU: every (layer, KV head) is independent, so more GPUs would each run "
-              "this same kernel on their share of heads with no communication; run with --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU: every (batch, layer, KV head) is independent, so N GPUs would each run "
+              "this same path on G/N of the heads with no communication. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     import torch
 
     import key_redundancy_scoring_amd as krs
-    from synth import get_config, make_heads
+    from synth import dirichlet_capacities, get_config, make_heads
 
-    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a ROCm GPU")
     dev = torch.device("cuda:0")
     cfg = get_config(args.config)
     if args.heads:
         cfg = cfg.with_(G=args.heads)
     G, N, d = cfg.G, cfg.N, cfg.d
-    removal = cfg.removal if cfg.removal is not None else 0.5
 
     t0 = time.perf_counter()
     K = torch.empty((G, N, d), dtype=torch.int16, device=dev)
@@ -107,8 +165,12 @@ def main():
     gen_s = time.perf_counter() - t0
     print(f"# generated and uploaded {G} heads in {gen_s:.1f} s", file=sys.stderr, flush=True)
 
-    cap = krs.uniform_capacity(N, removal)
-    caps = torch.full((G,), cap, dtype=torch.int32, device=dev)
+    if cfg.removal is not None:
+        cap_list = [krs.uniform_capacity(N, cfg.removal)] * G
+    else:
+        cap_list = [int(c) for c in dirichlet_capacities(cfg)]
+    caps = torch.tensor(cap_list, dtype=torch.int32, device=dev)
+    offsets = krs.capacity_offsets(cap_list, N)
     s_out, sel_out, rep_out = {}, {}, {}
     s_ws = r_ws = None
 
@@ -117,7 +179,8 @@ def main():
         r = krs.score(K, V, cfg.tau, cfg.window, cfg.sink, cfg.recent, out=s_out, ws=s_ws, events=ev_s)
         s_ws = r["ws"]
         s_out.update({k: r[k] for k in ("count", "best_sim", "best_idx", "energy", "score")})
-        sl = krs.select(r["score"], r["energy"], caps, cfg.sink, cfg.recent, out=sel_out, events=ev_sel)
+        sl = krs.select(r["score"], r["energy"], caps, cfg.sink, cfg.recent, out=sel_out, events=ev_sel,
+                        offsets=offsets)
         sel_out.update({"keep": sl["keep"], "kept_idx": sl["kept_idx"]})
         rp = krs.repair(K, sl["keep"], cfg.tau, cfg.window, cfg.sink, cfg.recent, out=rep_out, ws=r_ws, events=ev_r)
         r_ws = rp["ws"]
@@ -155,9 +218,18 @@ def main():
     dense = 2.0 * G * N * N * d
     achieved = alg / (gram_ms * 1e-3) / 1e12
     exec_tflops = dense / (gram_ms * 1e-3) / 1e12
-    rgram = restricted_gram_flops(N, cap, d, G)
+    mean_cap = float(np.mean(cap_list))
+    rgram = restricted_gram_flops(N, mean_cap, d, G)
     norms_bytes = G * N * (4 * d + 20)
 
+    traffic = None
+    meas = MEASURED_TRAFFIC.get(source_hash(GRAM_SOURCE))
+    if meas is not None and meas.get("workload") == (G, N, d):
+        traffic = meas["bytes_per_launch"]
+
+    twin = int(round(cfg.twin_frac * 100))
+    budget = (f"{int(round(cfg.removal * 100))}% removal" if cfg.removal is not None
+              else f"Dirichlet(1) split of a {int(round(cfg.budget_frac * 100))}% budget per group of {cfg.group} heads")
     line = {
         "metric": METRIC,
         "value": G * N / (ms_per_step * 1e-3),
@@ -171,15 +243,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: {G} heads x N={N} x d={d}, {int(cfg.twin_frac * 100)}% planted twins, "
-                               f"score+select+repair (repair of the selected set)",
+        "config": {"workload": f"{cfg.name}: {G} heads x N={N} x d={d}, {twin}% planted twins, tau {cfg.tau}, "
+                               f"window {cfg.window}, {budget}; score + select + repair of the selected set",
                    "G": G, "N": N, "d": d, "tau": cfg.tau, "window": cfg.window, "sink": cfg.sink,
-                   "recent": cfg.recent, "removal": removal, "capacity": cap, "parallelism": "single GPU"},
+                   "recent": cfg.recent, "mean_capacity": mean_cap, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "gram_kernel<64,score>", "algorithmic_flop_per_launch": alg,
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "kernel": f"gram_kernel<{d}, score>", "algorithmic_flop_per_launch": alg,
                      "avg_launch_ms": gram_ms},
-        "gram": {"dense_equiv_tflops": exec_tflops, "mfma_frac_executed": exec_tflops / PEAK_BF16_TFLOPS,
+        "gram": {"dense_equiv_tflops": exec_tflops, "mfma_frac_dense_equiv": exec_tflops / PEAK_BF16_TFLOPS,
                  "keys_per_s": G * N / (gram_ms * 1e-3), "ms": gram_ms},
         "phases_ms": {"norms_energy": norms_ms, "gram_score": gram_ms, "select": select_ms,
                       "repair_norms": r_norms_ms, "repair_compact": r_compact_ms, "repair_gram": r_gram_ms,
@@ -190,7 +262,7 @@ def main():
         "generation_s": gen_s,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_rows)
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -227,25 +227,31 @@ def capacity_offsets(capacity, N):
     return off
 
 
-def select(score_t, energy_t, capacity, sink=4, recent=64, out=None, events=None):
+def select(score_t, energy_t, capacity, sink=4, recent=64, out=None, events=None, offsets=None):
     """Exact-budget selection.  ``capacity``: int32 device tensor [G] (or a
-    host sequence, copied to the device).  Returns keep (uint8 [G][N]),
-    kept_idx (int32, heads concatenated, ascending within a head) and the
-    host-side offsets of each head's run."""
+    host sequence, copied to the device).  ``offsets`` (optional): the host
+    offsets ``capacity_offsets(capacity, N)``; passing them avoids reading a
+    device capacity back to the host.  Returns keep (uint8 [G][N]), kept_idx
+    (int32, heads concatenated, ascending within a head) and the host-side
+    offsets of each head's run."""
     lib = load()
     G, N = score_t.shape
     dev = score_t.device
     for t, nm in ((score_t, "score"), (energy_t, "energy")):
         if t.dtype != torch.float64 or not t.is_contiguous() or t.device != dev or tuple(t.shape) != (G, N):
             raise ValueError(f"{nm} must be contiguous float64 [G][N] on {dev}")
+    cap_host = None
     if not torch.is_tensor(capacity) or capacity.device != dev:
         cap_host = torch.as_tensor(capacity, dtype=torch.int32)
         capacity = cap_host.to(dev)
-    else:
-        cap_host = capacity.to("cpu")
     if capacity.dtype != torch.int32 or capacity.numel() != G or not capacity.is_contiguous():
         raise ValueError("capacity must be int32 [G]")
-    off = capacity_offsets(cap_host, N)
+    if offsets is not None:
+        off = torch.as_tensor(offsets, dtype=torch.int64)
+        if off.numel() != G + 1:
+            raise ValueError("offsets must have G + 1 entries")
+    else:
+        off = capacity_offsets(cap_host if cap_host is not None else capacity.to("cpu"), N)
     total = int(off[-1])
     out = {} if out is None else out
     keep = _need(out.get("keep"), (G, N), torch.uint8, dev, "keep")
