@@ -99,7 +99,7 @@ const char* twinkv_status_string(int status);
  *   best_sim[g][i] = max over j with |i-j| > window of sim(i,j), or -1 if no such j;
  *                    computed exactly in fp64 as dot/sqrt(n_i*n_j) for the chosen j
  *   best_idx[g][i] = the lowest j attaining best_sim, or -1 if no such j
- *   energy[g][i]   = ||v_i||^2, exact in fp64                            ([P2] 3.2)
+ *   energy[g][i]   = ||v_i||^2, fp64 sum of exact squares               ([P2] 3.2)
  *   score[g][i]    = energy * ln((N+1)/(count+1)), fp64                  ([P2] 3.2)
  *   omega[g][i]    = ln((N+1)/(count+1)) / ln(N+1) (optional: may be NULL)
  * where sim(i,j) = k_i.k_j / (||k_i|| ||k_j||) is the cosine of the

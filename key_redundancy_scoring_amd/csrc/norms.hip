@@ -6,9 +6,10 @@
 // normalises keys for the cosine of "TwinKV: A Composable Repair Pass ...",
 // section 3.2, Eq. 1.
 //
-// Products of two bf16 numbers are exact in fp32 (8-bit significands), and the
-// fp64 sum of d such products is exact for all but pathological exponent
-// spreads, so nsq and energy equal the exact real sums.
+// Products of two bf16 numbers are exact in fp32 (8-bit significands), so nsq
+// and energy are fp64 sums of d exact non-negative terms: exact when the
+// squares of a row span less than about 2^31 in magnitude, and otherwise
+// within (d-1) fp64 roundings of the exact sum.
 //
 // Layout: one key row is d bf16 = d/8 chunks of 16 bytes; d/8 consecutive
 // lanes read one row, so a wave reads 1 KiB of contiguous memory per load.
