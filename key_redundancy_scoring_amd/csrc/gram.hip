@@ -217,16 +217,48 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
     cnt[b] = 0;
   }
 
-  // ---- stage issue: direct loads into one LDS buffer, all addresses valid
+  // ---- byte offsets of this lane's stage loads and A-operand reads.  Load t
+  // of a stage reads column (tid + NT*t)/CH at a swizzled chunk, and the
+  // A operand of tile tt reads column 32*tt + lrow.  The swizzle repeats
+  // every 64 columns (d = 64) or 16 (d = 128), so the per-lane part of either
+  // address depends only on the parity of t or tt; the rest is a uniform
+  // stride (an SGPR base or an instruction offset).
+  static_assert((2 * NT / CH) % (CH == 8 ? 64 : 16) == 0 && 64 % (CH == 8 ? 64 : 16) == 0, "swizzle period");
+  uint32_t ld_off[2];
+  uint32_t a_off[2][KS];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int q = tid + NT * p;
+    const int c = q / CH;
+    ld_off[p] = (uint32_t)((c * CH + ((q % CH) ^ swz<CH>(c))) * 16 - p * NT * 16);
+    const int cp = 32 * p + lrow;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) a_off[p][s] = (uint32_t)((cp * CH + ((2 * s + h) ^ swz<CH>(cp))) * 16 - p * 32 * CH * 16);
+  }
+
+  // ---- stage issue: direct loads into one LDS buffer.  A stage whose
+  // columns all exist takes uniform bases and the per-lane offsets above; the
+  // last, partial stage clamps its columns to the last one (every address
+  // valid; the tiles past the end are masked).
   auto issue = [&](int col0, Stage<D, SC>& sb) TWINKV_INLINE {
+    if (col0 + SC <= ncols) {
+      const char* base = reinterpret_cast<const char*>(Cg + (size_t)col0 * CH);
+#pragma unroll
+      for (int t = 0; t < LOADS; ++t) dma16(base + (size_t)NT * 16 * t + ld_off[t & 1], &sb.keys[NT * t + wave * 64]);
+      if (wave < SC / 64) {
+        dma4(crinv_g + col0 + tid, &sb.rinv[wave * 64]);
+        if (MODE == GRAM_REPAIR) dma4(cpos_g + col0 + tid, &sb.pos[wave * 64]);
+      }
+      return;
+    }
     const int lastc = ncols - 1;
 #pragma unroll
     for (int t = 0; t < LOADS; ++t) {
-      const int q = tid + NT * t;  // LDS slot written by this lane
-      const int c = q / CH;
-      const int k = (q % CH) ^ swz<CH>(c);
-      const int col = col0 + c < lastc ? col0 + c : lastc;
-      dma16(Cg + (size_t)col * CH + k, &sb.keys[NT * t + wave * 64]);
+      // column tid/CH + (NT/CH)*t of the stage, chunk as in ld_off
+      const int c = col0 + tid / CH + (NT / CH) * t;
+      const int col = c < lastc ? c : lastc;
+      dma16(reinterpret_cast<const char*>(Cg + (size_t)col * CH) + (ld_off[t & 1] & (CH * 16 - 1)),
+            &sb.keys[NT * t + wave * 64]);
     }
     if (wave < SC / 64) {
       const int col = col0 + tid < lastc ? col0 + tid : lastc;
@@ -236,10 +268,12 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
   };
 
   // ---- per-tile pieces
-  auto load_a = [&](const Stage<D, SC>& sb, int tt, bf16x8 (&A)[KS]) TWINKV_INLINE {
-    const int ca = tt * 32 + lrow;  // this lane's A-operand column
+  // par = tt & 1
+  auto load_a = [&](const Stage<D, SC>& sb, int tt, int par, bf16x8 (&A)[KS]) TWINKV_INLINE {
+    const char* kb = reinterpret_cast<const char*>(sb.keys) + tt * 32 * CH * 16;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) A[s] = __builtin_bit_cast(bf16x8, sb.keys[ca * CH + ((2 * s + h) ^ swz<CH>(ca))]);
+    for (int s = 0; s < KS; ++s)
+      A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + (par ? a_off[1][s] : a_off[0][s])));
   };
   auto load_rv = [&](const Stage<D, SC>& sb, int tt, float (&rv)[16]) TWINKV_INLINE {
 #pragma unroll
@@ -334,7 +368,7 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
   __syncthreads();
   if (nstages > 1) issue(SC, buf1);
   if (nstages > 0) {
-    load_a(buf0, 0, A);
+    load_a(buf0, 0, 0, A);
 #pragma unroll
     for (int b = 0; b < RB; ++b) mfma_block(A, b, acc[b]);
     load_rv(buf0, 0, rv);
@@ -350,7 +384,7 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
 #pragma unroll 1
     for (int tt = 0; tt < TILES - 1; ++tt) {
       const int tile = st * TILES + tt;
-      load_a(cur, tt + 1, A);
+      load_a(cur, tt + 1, (tt + 1) & 1, A);
       load_rv(cur, tt + 1, rv_next);
       const float neg = ((mbits >> tt) & 1u) ? -__builtin_inff() : __builtin_inff();
 #pragma unroll
@@ -368,7 +402,7 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
     __syncthreads();
     if (st + 2 < nstages) issue((st + 2) * SC, cur);
     if (more) {
-      load_a(nxt, 0, A);
+      load_a(nxt, 0, 0, A);
       load_rv(nxt, 0, rv_next);
     }
     const int tile = st * TILES + TILES - 1;
