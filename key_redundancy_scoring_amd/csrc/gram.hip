@@ -477,14 +477,16 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
     }
   }
 
-  // ---- exact fp64 fixup of the best twin, merge of half-waves, outputs
-  // (unrolled: the per-block state stays in registers).  Each half-wave
-  // holds, for its row, the fp32 maximum over its 16 columns of every tile
-  // and the first tile attaining it.  Only a half whose maximum can be the
-  // row's looks at its candidates; it screens the 16 candidates with fp32
-  // dot products (v_dot2 of bf16 pairs) and evaluates exactly in fp64 only
-  // those within a safe margin of the largest, which always include the
-  // exact maximum.
+  // ---- exact fp64 fixup of the best twin and outputs (unrolled: the
+  // per-block state stays in registers).  Each half-wave holds, for its row,
+  // the fp32 maximum over its 16 columns of every tile and the first tile
+  // attaining it.  Only a half whose maximum can be the row's is looked at:
+  // its 16 candidates are screened with fp32 dot products and those within a
+  // safe margin of the largest, which always include the exact maximum, are
+  // evaluated exactly in fp64.  Both lanes of the row do the work, each over
+  // the feature chunks it holds as MFMA operands (chunks 2s+h), and
+  // add their partial sums: the two lanes obtain identical values and
+  // decisions, so the row's result needs no further merge.
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     const int i = row0 + 32 * b + lrow;
@@ -498,55 +500,80 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
     const float margin = 8e-5f * (float)sqrt(ni) + 1e-30f;
     const float other = __shfl_xor(best[b], 32);
     const bool look = row_ok && btile[b] >= 0 && best[b] >= other - margin;
-    if (look) {
-      const uint4* ki = Kg + (size_t)i * CH;
-      uint4 kr[CH];
+    const bool look_o = __shfl_xor((int)look, 32) != 0;
+    const int tile_o = __shfl_xor(btile[b], 32);
 #pragma unroll
-      for (int k = 0; k < CH; ++k) kr[k] = ki[k];
-      float ya[16];
-      float ymax = -__builtin_inff();
-#pragma unroll 4
-      for (int r = 0; r < 16; ++r) {
-        const int col = btile[b] * 32 + tile_col(r, h);
-        const int cc = col < ncols ? col : ncols - 1;
-        const int j = (MODE == GRAM_REPAIR) ? cpos_g[cc] : cc;
-        const int dist = i > j ? i - j : j - i;
-        const uint4* kj = Kg + (size_t)j * CH;
-        float dotf = 0.0f;
+    for (int p = 0; p < 2; ++p) {
+      const bool lk = (h == p) ? look : look_o;  // same in both lanes of the row
+      const int tp = (h == p) ? btile[b] : tile_o;
+      if (__ballot(lk) == 0ull) continue;
+      if (lk) {
+        // this lane's feature chunks of row i, reloaded (the sweep's copy is
+        // not kept alive this long)
+        uint4 kr[KS];
 #pragma unroll
-        for (int k = 0; k < CH; ++k) {
-          const uint4 q = kj[k];
-          dotf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[k].x), __builtin_bit_cast(bf16x2, q.x), dotf, false);
-          dotf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[k].y), __builtin_bit_cast(bf16x2, q.y), dotf, false);
-          dotf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[k].z), __builtin_bit_cast(bf16x2, q.z), dotf, false);
-          dotf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[k].w), __builtin_bit_cast(bf16x2, q.w), dotf, false);
+        for (int s2 = 0; s2 < KS; ++s2) kr[s2] = Kg[(size_t)i * CH + 2 * s2 + h];
+        constexpr int BATCH = CH == 8 ? 4 : 2;
+        float ya[16];
+        float ymax = -__builtin_inff();
+#pragma unroll
+        for (int r0 = 0; r0 < 16; r0 += BATCH) {
+          uint4 q[BATCH][KS];
+          float rj[BATCH];
+#pragma unroll
+          for (int u = 0; u < BATCH; ++u) {
+            const int col = tp * 32 + tile_col(r0 + u, p);
+            const int cc = col < ncols ? col : ncols - 1;
+            const int j = (MODE == GRAM_REPAIR) ? cpos_g[cc] : cc;
+            const uint4* kj = Kg + (size_t)j * CH;
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2) q[u][s2] = kj[2 * s2 + h];
+            rj[u] = crinv_g[cc];
+          }
+#pragma unroll
+          for (int u = 0; u < BATCH; ++u) {
+            const int col = tp * 32 + tile_col(r0 + u, p);
+            const int cc = col < ncols ? col : ncols - 1;
+            const int j = (MODE == GRAM_REPAIR) ? cpos_g[cc] : cc;
+            const int dist = i > j ? i - j : j - i;
+            float part = 0.0f;
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2) {
+              part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[s2].x), __builtin_bit_cast(bf16x2, q[u][s2].x), part, false);
+              part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[s2].y), __builtin_bit_cast(bf16x2, q[u][s2].y), part, false);
+              part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[s2].z), __builtin_bit_cast(bf16x2, q[u][s2].z), part, false);
+              part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[s2].w), __builtin_bit_cast(bf16x2, q[u][s2].w), part, false);
+            }
+            const float dotf = part + __shfl_xor(part, 32);
+            ya[r0 + u] = (col < ncols && dist > w) ? dotf * rj[u] : -__builtin_inff();
+            ymax = __builtin_fmaxf(ymax, ya[r0 + u]);
+          }
         }
-        ya[r] = (col < ncols && dist > w) ? dotf * crinv_g[cc] : -__builtin_inff();
-        ymax = __builtin_fmaxf(ymax, ya[r]);
-      }
+        // the candidates as a bit set (invalid ones are -inf); the loop runs
+        // as often as the most candidates any lane has, usually once or twice
+        unsigned cm = 0u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cm |= (ya[r] > -__builtin_inff() && ya[r] >= ymax - margin) ? 1u << r : 0u;
 #pragma unroll 1
-      for (int r = 0; r < 16; ++r) {
-        if (!(ya[r] > -__builtin_inff() && ya[r] >= ymax - margin)) continue;  // invalid ones are -inf
-        const int col = btile[b] * 32 + tile_col(r, h);
-        const int j = (MODE == GRAM_REPAIR) ? cpos_g[col] : col;
-        const uint4* kj = Kg + (size_t)j * CH;
-        double dot = 0.0;
+        while (cm != 0u) {
+          const int r = __builtin_ctz(cm);
+          cm &= cm - 1u;
+          const int col = tp * 32 + 8 * (r >> 2) + 4 * p + (r & 3);
+          const int j = (MODE == GRAM_REPAIR) ? cpos_g[col] : col;
+          const uint4* kj = Kg + (size_t)j * CH;
+          double part = 0.0;
 #pragma unroll
-        for (int k = 0; k < CH; ++k) dot += dot8_exact(kr[k], kj[k]);
-        const double nn = ni * a.nsq[(size_t)g * N + j];
-        double sim = nn > 0.0 ? dot / sqrt(nn) : 0.0;
-        sim += 0.0;
-        if (aa < 0 || sim > bb || (sim == bb && j < aa)) {
-          bb = sim;
-          aa = j;
+          for (int s2 = 0; s2 < KS; ++s2) part += dot8_exact(kr[s2], kj[2 * s2 + h]);
+          const double dot = part + __shfl_xor(part, 32);
+          const double nn = ni * a.nsq[(size_t)g * N + j];
+          double sim = nn > 0.0 ? dot / sqrt(nn) : 0.0;
+          sim += 0.0;
+          if (aa < 0 || sim > bb || (sim == bb && j < aa)) {
+            bb = sim;
+            aa = j;
+          }
         }
       }
-    }
-    const double pb = __shfl_xor(bb, 32);
-    const int pa = __shfl_xor(aa, 32);
-    if (pa >= 0 && (aa < 0 || pb > bb || (pb == bb && pa < aa))) {
-      bb = pb;
-      aa = pa;
     }
     int c = 0;
     if (MODE == GRAM_SCORE) c = cnt[b] + __shfl_xor(cnt[b], 32);
