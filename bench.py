@@ -13,7 +13,8 @@ Llama-3.2-1B shape: 16 layers x 8 KV heads = 128 heads, N = 32768, head dim
 removal.
 
 Prints one JSON line.  `value` is keys (head positions) through the whole path
-per second.  `roofline` is for the dominant kernel, the score-mode Gram
+per second.  `gather_kv` times, outside the step, the packed cache of the
+last step's selection (retained keys and values in sequence order).  `roofline` is for the dominant kernel, the score-mode Gram
 sweep, timed with HIP events that the library records around its launch on
 the stream it runs on; its `achieved` counts the algorithmic work, one
 d-length dot product (2d flop) per unordered nonlocal pair, while `gram`
@@ -214,6 +215,21 @@ def main():
         for x in e:
             x.close()
 
+    # packed cache of the last step's selection (not part of the timed step)
+    gev = [krs.Events(2) for _ in range(args.steps)]
+    gout = {}
+    offsets_dev = torch.as_tensor(offsets, dtype=torch.int64).to(dev)
+    for k in range(args.steps + 1):
+        gres = krs.gather_kv(K, V, sel_out["kept_idx"], offsets_dev, total=int(offsets[-1]), out=gout,
+                             events=gev[k - 1] if k else None)
+        gout = {"keys": gres["keys"], "values": gres["values"]}
+    torch.cuda.synchronize()
+    gather_ms = float(np.mean([e.elapsed_ms(0, 1) for e in gev]))
+    for e in gev:
+        e.close()
+    gather_rows = gres["total"]
+    gather_bytes = gather_rows * (8 * d + 4)
+
     alg = algorithmic_gram_flops(N, d, cfg.window, G)
     dense = 2.0 * G * N * N * d
     achieved = alg / (gram_ms * 1e-3) / 1e12
@@ -258,6 +274,9 @@ def main():
                       "repair_swap": r_swap_ms},
         "phase_rates": {"norms_energy_GBs": norms_bytes / (norms_ms * 1e-3) / 1e9,
                         "repair_gram_dense_tflops": rgram / (r_gram_ms * 1e-3) / 1e12},
+        "gather_kv": {"ms": gather_ms, "rows": gather_rows, "algorithmic_bytes": gather_bytes,
+                      "GBs": gather_bytes / (gather_ms * 1e-3) / 1e9,
+                      "frac_hbm": gather_bytes / (gather_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
         "swaps_total": int(rep_out["n_swaps"].sum().item()),
         "generation_s": gen_s,
     }

@@ -11,7 +11,9 @@
  *   twinkv_select  exact-budget per-head retention with protected sink and
  *                  recent positions;
  *   twinkv_repair  the one-shot orphan/donor swap on a given retained set at
- *                  a fixed budget.
+ *                  a fixed budget;
+ *   twinkv_gather_kv  the packed, unpadded cache of the retained keys and
+ *                  values in sequence order.
  *
  * Sources (page title and section/equation):
  *   [P1] "TwinKV: A Composable Repair Pass for KV Cache Eviction via Pairwise
@@ -19,7 +21,8 @@
  *        protected regions), section 3.4 (Eq. 4, orphans, donors, swap).
  *   [P2] "Small Frequency Corrections Can Change What Survives KV Cache
  *        Compression" (paperpeel): section 3.1 (budget, protection), section
- *        3.2 (count, energy, score, ties), section 3.4 (selection order).
+ *        3.2 (count, energy, score, ties), section 3.4 (selection order and
+ *        physical cache layout).
  *
  * Conventions for every entry point:
  *   - Array arguments are DEVICE pointers owned by the caller; the library
@@ -80,7 +83,7 @@ typedef struct twinkv_params {
 enum { TWINKV_OP_SCORE = 0, TWINKV_OP_SELECT = 1, TWINKV_OP_REPAIR = 2 };
 
 /* Phase counts for the `marks` argument. */
-enum { TWINKV_SCORE_PHASES = 2, TWINKV_SELECT_PHASES = 1, TWINKV_REPAIR_PHASES = 4 };
+enum { TWINKV_SCORE_PHASES = 2, TWINKV_SELECT_PHASES = 1, TWINKV_REPAIR_PHASES = 4, TWINKV_GATHER_PHASES = 1 };
 
 /* Bytes of workspace an operation needs for these parameters; 0 if the
  * parameters are invalid (see the entry points) or the op needs none. */
@@ -158,6 +161,31 @@ int twinkv_repair(const twinkv_params* params, const void* keys, const uint8_t* 
                   uint8_t* keep_out, double* best_sim, int32_t* best_idx, int32_t* n_orphans,
                   int32_t* n_donors, int32_t* n_swaps, int32_t* swap_pairs, void* workspace,
                   size_t workspace_bytes, hipStream_t stream, hipEvent_t* marks);
+
+/*
+ * twinkv_gather_kv - physical cache layout of a selection ([P2] section 3.4):
+ * the retained keys (and values) of every head, in sequence order, packed
+ * head after head with no padding.  Head g's retained positions are
+ * kept_idx[kept_off[g] .. kept_off[g+1]) (ascending, as twinkv_select writes
+ * them); row kept_off[g] + r of out_keys / out_values is row kept_idx[kept_off[g]
+ * + r] of head g, copied bit for bit (keys are not re-rotated, values are
+ * unchanged).  Heads with equal quotas therefore form contiguous slices of
+ * one tensor and the payload is exactly 2 * d * total elements.
+ *   keys, values:  bf16 [G][N][d] (values may be NULL: keys only)
+ *   kept_idx:      int32 [total]
+ *   kept_off:      int64 [G+1] device array, kept_off[0] = 0 and
+ *                  kept_off[g+1] - kept_off[g] = that head's count (0..N),
+ *                  kept_off[G] = total
+ *   out_keys, out_values: bf16 [total][d] (out_values NULL iff values NULL;
+ *                  both may be NULL when total is 0)
+ * Of the parameters only G, N and d are read.  The kernel clamps every
+ * offset and index to [0, total] / [0, N), so inconsistent offsets produce
+ * wrong rows, never an access outside the stated sizes.
+ * Phases for `marks`: 0 = gather.
+ */
+int twinkv_gather_kv(const twinkv_params* params, const void* keys, const void* values, const int32_t* kept_idx,
+                     const int64_t* kept_off, int64_t total, void* out_keys, void* out_values, hipStream_t stream,
+                     hipEvent_t* marks);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "twinkv.h")
 
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 OP_SCORE, OP_SELECT, OP_REPAIR = 0, 1, 2
-SCORE_PHASES, SELECT_PHASES, REPAIR_PHASES = 2, 1, 4
+SCORE_PHASES, SELECT_PHASES, REPAIR_PHASES, GATHER_PHASES = 2, 1, 4, 1
 
 
 class Params(ctypes.Structure):
@@ -68,6 +68,8 @@ def load():
     lib.twinkv_select.restype = ctypes.c_int
     lib.twinkv_repair.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.twinkv_repair.restype = ctypes.c_int
+    lib.twinkv_gather_kv.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp, vp]
+    lib.twinkv_gather_kv.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -297,3 +299,41 @@ def repair(keys, keep_in, tau, window, sink=4, recent=64, out=None, ws=None, eve
     _check(st, "twinkv_repair")
     o["ws"] = ws
     return o
+
+
+def gather_kv(keys, values, kept_idx, offsets, out=None, events=None, total=None):
+    """Packed cache of the retained positions: the rows kept_idx[off[g]:off[g+1]]
+    of every head g, in that order, for keys (and values unless None).
+    ``offsets``: int64 [G+1] prefix sums of the per-head counts, on the host
+    (copied to the device) or on the keys' device; ``total`` (optional) is
+    offsets[G], which saves reading device offsets back.  Returns out_keys (and
+    out_values) [total][d] device tensors of the inputs' dtypes, plus the
+    device offsets under "offsets"."""
+    lib = load()
+    keys = _as_bf16_bits(keys, "keys")
+    G, N, d = keys.shape
+    dev = keys.device
+    if values is not None:
+        values = _as_bf16_bits(values, "values")
+        if values.shape != keys.shape:
+            raise ValueError("keys and values must have the same shape")
+    off = torch.as_tensor(offsets, dtype=torch.int64)
+    if off.numel() != G + 1:
+        raise ValueError("offsets must have G + 1 entries")
+    off_dev = off if off.device == dev else off.to(dev)
+    if total is None:
+        total = int(off[-1]) if off.device.type == "cpu" else int(off_dev[-1].item())
+    total = int(total)
+    if kept_idx.dtype != torch.int32 or kept_idx.device != dev or not kept_idx.is_contiguous() \
+            or kept_idx.numel() < total:
+        raise ValueError("kept_idx must be a contiguous int32 device tensor with at least total entries")
+    out = {} if out is None else out
+    ok = _need(out.get("keys"), (total, d), keys.dtype, dev, "out keys")
+    ov = _need(out.get("values"), (total, d), values.dtype, dev, "out values") if values is not None else None
+    p = params(G, N, d, 0.0, 0, 0, 0)  # gather reads only G, N, d
+    st = lib.twinkv_gather_kv(ctypes.byref(p), _ptr(keys), _ptr(values), _ptr(kept_idx), _ptr(off_dev), total,
+                              _ptr(ok) if total else ctypes.c_void_p(0),
+                              (_ptr(ov) if total else ctypes.c_void_p(0)) if values is not None else ctypes.c_void_p(0),
+                              _stream(), _marks(events, GATHER_PHASES))
+    _check(st, "twinkv_gather_kv")
+    return {"keys": ok, "values": ov, "offsets": off_dev, "total": total}

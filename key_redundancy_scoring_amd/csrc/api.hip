@@ -168,6 +168,26 @@ int twinkv_select(const twinkv_params* p, const double* score, const double* ene
   return TWINKV_OK;
 }
 
+int twinkv_gather_kv(const twinkv_params* p, const void* keys, const void* values, const int32_t* kept_idx,
+                     const int64_t* kept_off, int64_t total, void* out_keys, void* out_values, hipStream_t stream,
+                     hipEvent_t* marks) {
+  TRY(check_sizes(p));
+  if (p->d != 64 && p->d != 128) return TWINKV_ERR_UNSUPPORTED;
+  if (!keys || !kept_off || total < 0) return TWINKV_ERR_ARG;
+  if (total > p->G * p->N) return TWINKV_ERR_ARG;
+  if (total > 0 && (!kept_idx || !out_keys)) return TWINKV_ERR_ARG;
+  if (total > 0 && (values == nullptr) != (out_values == nullptr)) return TWINKV_ERR_ARG;
+  if (!aligned16(keys) || (values && !aligned16(values)) || (out_keys && !aligned16(out_keys)) ||
+      (out_values && !aligned16(out_values)))
+    return TWINKV_ERR_ARG;
+  TRY(record(marks, 0, stream));
+  TRY_HIP(launch_gather_kv(static_cast<const uint16_t*>(keys), static_cast<const uint16_t*>(values), kept_idx,
+                           kept_off, p->G, p->N, p->d, total, static_cast<uint16_t*>(out_keys),
+                           static_cast<uint16_t*>(out_values), stream));
+  TRY(record(marks, 1, stream));
+  return TWINKV_OK;
+}
+
 int twinkv_repair(const twinkv_params* p, const void* keys, const uint8_t* keep_in, uint8_t* keep_out,
                   double* best_sim, int32_t* best_idx, int32_t* n_orphans, int32_t* n_donors, int32_t* n_swaps,
                   int32_t* swap_pairs, void* workspace, size_t workspace_bytes, hipStream_t stream,

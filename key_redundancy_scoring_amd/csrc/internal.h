@@ -54,6 +54,13 @@ hipError_t launch_compact(const uint8_t* keep_in, int64_t G, int64_t N, int32_t*
 hipError_t launch_gather(const uint16_t* keys, const float* rinv, const int32_t* pos, const int32_t* ncols, int64_t G,
                          int64_t N, int d, uint16_t* ckeys, float* crinv, hipStream_t stream);
 
+// Pack the retained keys (and values, if not null) of every head in sequence
+// order: head g's rows kept_idx[kept_off[g] .. kept_off[g+1]) go to rows
+// kept_off[g].. of out_keys / out_values ([total][d]).
+hipError_t launch_gather_kv(const uint16_t* keys, const uint16_t* values, const int32_t* kept_idx,
+                            const int64_t* kept_off, int64_t G, int64_t N, int d, int64_t total, uint16_t* out_keys,
+                            uint16_t* out_values, hipStream_t stream);
+
 struct SwapArgs {
   const uint8_t* keep_in;
   const double* best;

@@ -15,7 +15,8 @@ Sources (cited by page title and section / equation; no line numbers):
 * [P2] "Small Frequency Corrections Can Change What Survives KV Cache
   Compression" (paperpeel page): section 3.1 exact budget and protected
   positions, section 3.2 value-weighted nonlocal key rarity (count, value
-  energy, discounted score, tie rule), section 3.4 selection in sequence order,
+  energy, discounted score, tie rule), section 3.4 selection in sequence order
+  and the packed, unpadded cache layout,
   appendix A.1 boundary handling and the Figure 3 example.
 
 Every quantity is evaluated straight from its definition in float64.  Keys and
@@ -285,6 +286,35 @@ def repair_head(K: np.ndarray, retained: np.ndarray, tau: float, window: int, si
         "m": int(m),
         "pairs": pairs.astype(np.int64),
     }
+
+
+# ----------------------------------------------------------------------------
+# [P2] section 3.4: physical cache layout of a selection
+
+
+def pack_retained(K: np.ndarray, V: np.ndarray | None, kept: list):
+    """The retained keys (and values) of every head in sequence order, heads
+    one after another with no padding ([P2] section 3.4): head g contributes
+    rows K[g][kept[g]] (kept[g] ascending), copied unchanged.  ``K``, ``V``:
+    [G][N][d] arrays (bf16 bit patterns or any dtype; copied as they are).
+    Returns (K_packed [total][d], V_packed or None, offsets int64 [G+1])."""
+    G = K.shape[0]
+    if len(kept) != G:
+        raise ValueError("one retained list per head")
+    offsets = np.zeros(G + 1, dtype=np.int64)
+    kp, vp = [], []
+    for g in range(G):
+        idx = np.asarray(kept[g], dtype=np.int64)
+        if idx.size and (np.any(np.diff(idx) <= 0) or idx[0] < 0 or idx[-1] >= K.shape[1]):
+            raise ValueError("retained positions must be ascending and within the prefix")
+        offsets[g + 1] = offsets[g] + idx.size
+        kp.append(K[g][idx])
+        if V is not None:
+            vp.append(V[g][idx])
+    d = K.shape[2]
+    Kp = np.concatenate(kp, axis=0) if kp else np.zeros((0, d), K.dtype)
+    Vp = (np.concatenate(vp, axis=0) if vp else np.zeros((0, d), V.dtype)) if V is not None else None
+    return Kp, Vp, offsets
 
 
 # ----------------------------------------------------------------------------

@@ -16,8 +16,8 @@ FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: every call belo
 def test_library_exports_every_header_symbol():
     lib = krs.load()
     declared = krs.header_symbols()
-    assert declared == ["twinkv_repair", "twinkv_score", "twinkv_select", "twinkv_status_string",
-                        "twinkv_uniform_capacity", "twinkv_workspace_bytes"]
+    assert declared == ["twinkv_gather_kv", "twinkv_repair", "twinkv_score", "twinkv_select",
+                        "twinkv_status_string", "twinkv_uniform_capacity", "twinkv_workspace_bytes"]
     for name in declared:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
@@ -106,3 +106,24 @@ def test_params_struct_layout():
     assert ctypes.sizeof(L.Params) == 40
     assert [L.Params.G.offset, L.Params.N.offset, L.Params.d.offset, L.Params.window.offset, L.Params.tau.offset,
             L.Params.sink.offset, L.Params.recent.offset] == [0, 8, 16, 20, 24, 32, 36]
+
+
+def test_gather_validation():
+    lib = krs.load()
+    p = L.params(2, 8, 64, 0.0, 0)
+    # only refusals are exercised: each fails validation before any launch
+    bad = [
+        (L.params(2, 8, 32, 0.0, 0), FAKE, None, FAKE, FAKE, 4, FAKE, None, L.ERR_UNSUPPORTED),
+        (p, None, None, FAKE, FAKE, 4, FAKE, None, L.ERR_ARG),          # no keys
+        (p, FAKE, None, FAKE, None, 4, FAKE, None, L.ERR_ARG),          # no offsets
+        (p, FAKE, None, FAKE, FAKE, -1, FAKE, None, L.ERR_ARG),         # negative total
+        (p, FAKE, None, FAKE, FAKE, 17, FAKE, None, L.ERR_ARG),         # total above G*N
+        (p, FAKE, None, None, FAKE, 4, FAKE, None, L.ERR_ARG),          # no kept_idx
+        (p, FAKE, None, FAKE, FAKE, 4, None, None, L.ERR_ARG),          # no output
+        (p, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None, L.ERR_ARG),          # values without their output
+        (p, FAKE, None, FAKE, FAKE, 4, FAKE, FAKE, L.ERR_ARG),          # output without values
+        (p, ctypes.c_void_p(0x100008), None, FAKE, FAKE, 4, FAKE, None, L.ERR_ARG),  # misaligned
+        (L.params(0, 8, 64, 0.0, 0), FAKE, None, FAKE, FAKE, 0, FAKE, None, L.ERR_ARG),
+    ]
+    for pp, k, v, idx, off, total, ok_, ov, want in bad:
+        assert lib.twinkv_gather_kv(ctypes.byref(pp), k, v, idx, off, total, ok_, ov, None, None) == want

@@ -9,6 +9,8 @@ three ways:
   is cheap) and seeded row samples of further heads that include the sink /
   recent boundaries and the last row block;
 * value energy against the oracle for every head;
+* the packed cache of host-drawn retained sets of the workload's quotas,
+  bit for bit against the oracle for every head;
 * properties that hold at any size for every head: planted near-duplicate
   clusters lower-bound the counts, every best twin is a valid nonlocal
   position, the selection keeps exactly its capacity with protection and a
@@ -27,6 +29,7 @@ import key_redundancy_scoring_amd as krs
 from oracle import twinkv_oracle as O
 from synth import dirichlet_capacities, get_config, gumbel_retained, make_heads
 from tests import parity as PR
+from tests.test_gpu_gather import check_gather
 
 pytestmark = pytest.mark.gpu
 
@@ -216,6 +219,10 @@ def _score_select_suite(cfg, caps, whole_heads, row_heads, repair_selected, tag)
         _row_checks(K[g], V[g], g, cfg, res, tag)
     for g in whole_heads:
         _oracle_head_checks(K[g], V[g], g, cfg, res, sel, rep, int(caps[g]), tag)
+    # packed cache of host-drawn retained sets of the same quotas, every head
+    kept = [np.flatnonzero(gumbel_retained(cfg, g, keep=int(caps[g]))) for g in range(cfg.G)]
+    total = check_gather(K, V, kept, tag=tag)
+    _say(f"[{tag}] packed cache of {total} rows bit-exact")
 
 
 def test_fullsize_llama32_1b_32k():

@@ -435,3 +435,43 @@ def test_repair_idempotent_when_twins_touch_protected_positions():
         r1 = O.repair_head(K, S0, 0.9, w, sink, recent)
         r2 = O.repair_head(K, r1["keep"], 0.9, w, sink, recent)
         assert r2["m"] == 0 and np.array_equal(r2["keep"], r1["keep"])
+
+
+# ---------------------------------------------------------------------------
+# physical cache layout (section 3.4 of the frequency-correction page)
+
+
+def test_pack_retained_hand_example():
+    """Two heads, five positions, d = 2: head 0 keeps {0, 3}, head 1 keeps
+    {1, 2, 4}; rows come out in sequence order, head 0 first, no padding."""
+    K = np.arange(2 * 5 * 2, dtype=np.uint16).reshape(2, 5, 2)
+    V = (1000 + np.arange(2 * 5 * 2)).astype(np.uint16).reshape(2, 5, 2)
+    Kp, Vp, off = O.pack_retained(K, V, [[0, 3], [1, 2, 4]])
+    assert off.tolist() == [0, 2, 5]
+    assert Kp.tolist() == [[0, 1], [6, 7], [12, 13], [14, 15], [18, 19]]
+    assert Vp.tolist() == [[1000, 1001], [1006, 1007], [1012, 1013], [1014, 1015], [1018, 1019]]
+
+
+def test_pack_retained_payload_matches_budget_example():
+    """The payload is exactly 2*d*sum(b_h) elements; with the two-head example
+    capacities (202, 310) that is 2*d*H*B for H = 2, B = 256 (budget
+    conservation), and each packed row equals its source row bit for bit."""
+    g = _golden("budget_conservation.json")
+    rng = np.random.default_rng(5)
+    N, d = g["N"], 64
+    K = rng.integers(0, 1 << 16, size=(2, N, d), dtype=np.uint16)
+    V = rng.integers(0, 1 << 16, size=(2, N, d), dtype=np.uint16)
+    kept = [np.sort(rng.choice(N, c, replace=False)) for c in g["capacities"]]
+    Kp, Vp, off = O.pack_retained(K, V, kept)
+    assert Kp.size + Vp.size == 2 * d * sum(g["capacities"]) == 2 * d * 2 * g["B"]
+    for h in range(2):
+        rows = slice(off[h], off[h + 1])
+        assert np.array_equal(Kp[rows], K[h][kept[h]]) and np.array_equal(Vp[rows], V[h][kept[h]])
+
+
+def test_pack_retained_rejects_unordered_and_handles_empty():
+    K = np.zeros((2, 4, 8), np.uint16)
+    with pytest.raises(ValueError):
+        O.pack_retained(K, None, [[2, 1], []])
+    Kp, Vp, off = O.pack_retained(K, None, [[], []])
+    assert Kp.shape == (0, 8) and Vp is None and off.tolist() == [0, 0, 0]
