@@ -14,7 +14,9 @@ removal.
 
 Prints one JSON line.  `value` is keys (head positions) through the whole path
 per second.  `gather_kv` times, outside the step, the packed cache of the
-last step's selection (retained keys and values in sequence order).  `roofline` is for the dominant kernel, the score-mode Gram
+last step's selection (retained keys and values in sequence order), and
+`allocate` the per-head capacities from the attention of the last 32
+synthetic prefix queries of each KV head (8 KV heads per layer).  `roofline` is for the dominant kernel, the score-mode Gram
 sweep, timed with HIP events that the library records around its launch on
 the stream it runs on; its `achieved` counts the algorithmic work, one
 d-length dot product (2d flop) per unordered nonlocal pair, while `gram`
@@ -42,6 +44,7 @@ if ROOT not in sys.path:
 METRIC = "keys scored/sec + Gram TFLOP/s (MFMA % of peak) at N=32k, 1 MI355X"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU (published: 2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0
+PEAK_FP64_TFLOPS = 78.6
 GRAM_SOURCE = os.path.join(ROOT, "key_redundancy_scoring_amd", "csrc", "gram.hip")
 
 # HBM traffic of one score-mode Gram launch on the default workload, from
@@ -230,6 +233,27 @@ def main():
     gather_rows = gres["total"]
     gather_bytes = gather_rows * (8 * d + 4)
 
+    # per-head capacities from prefix attention, 8 KV heads per layer
+    # (not part of the timed step)
+    from synth import make_queries
+    Qh = torch.from_numpy(np.stack([make_queries(cfg, g) for g in range(G)]).view(np.int16)).to(dev)
+    Hkv = 8 if G % 8 == 0 else 1
+    B_alloc = krs.uniform_capacity(N, cfg.removal if cfg.removal is not None else 0.5)
+    aev = [krs.Events(4) for _ in range(args.steps)]
+    aout, aws = {}, None
+    for k in range(args.steps + 1):
+        ares = krs.allocate(K, Qh, Hkv, B_alloc, cfg.sink, cfg.recent, out=aout, ws=aws,
+                            events=aev[k - 1] if k else None)
+        aws = ares["ws"]
+        aout = {kk: ares[kk] for kk in ("capacity", "g_count", "z")}
+    torch.cuda.synchronize()
+    alloc_ms = [float(np.mean([e.elapsed_ms(a, a + 1) for e in aev])) for a in range(3)]
+    for e in aev:
+        e.close()
+    nq = Qh.shape[1] * Qh.shape[2]
+    logit_flops = 2.0 * G * nq * N * d  # one fp64 dot product per (query, key)
+    del Qh
+
     alg = algorithmic_gram_flops(N, d, cfg.window, G)
     dense = 2.0 * G * N * N * d
     achieved = alg / (gram_ms * 1e-3) / 1e12
@@ -277,6 +301,10 @@ def main():
         "gather_kv": {"ms": gather_ms, "rows": gather_rows, "algorithmic_bytes": gather_bytes,
                       "GBs": gather_bytes / (gather_ms * 1e-3) / 1e9,
                       "frac_hbm": gather_bytes / (gather_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "allocate": {"ms": sum(alloc_ms), "stats_ms": alloc_ms[0], "aggregate_pool_ms": alloc_ms[1],
+                     "rank_eq5_ms": alloc_ms[2], "heads_per_layer": Hkv, "queries_per_head": nq,
+                     "logit_fp64_tflops": logit_flops / (alloc_ms[0] * 1e-3) / 1e12,
+                     "frac_fp64_peak": logit_flops / (alloc_ms[0] * 1e-3) / 1e12 / PEAK_FP64_TFLOPS},
         "swaps_total": int(rep_out["n_swaps"].sum().item()),
         "generation_s": gen_s,
     }

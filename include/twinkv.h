@@ -13,7 +13,9 @@
  *   twinkv_repair  the one-shot orphan/donor swap on a given retained set at
  *                  a fixed budget;
  *   twinkv_gather_kv  the packed, unpadded cache of the retained keys and
- *                  values in sequence order.
+ *                  values in sequence order;
+ *   twinkv_allocate  per-head capacities of a layer from the attention of
+ *                  its last observed prefix queries.
  *
  * Sources (page title and section/equation):
  *   [P1] "TwinKV: A Composable Repair Pass for KV Cache Eviction via Pairwise
@@ -21,8 +23,9 @@
  *        protected regions), section 3.4 (Eq. 4, orphans, donors, swap).
  *   [P2] "Small Frequency Corrections Can Change What Survives KV Cache
  *        Compression" (paperpeel): section 3.1 (budget, protection), section
- *        3.2 (count, energy, score, ties), section 3.4 (selection order and
- *        physical cache layout).
+ *        3.2 (count, energy, score, ties), section 3.3 (head allocation,
+ *        Equation 5), section 3.4 (selection order and physical cache
+ *        layout), appendices A.2, A.3 (prefix attention, budget proof).
  *
  * Conventions for every entry point:
  *   - Array arguments are DEVICE pointers owned by the caller; the library
@@ -83,7 +86,8 @@ typedef struct twinkv_params {
 enum { TWINKV_OP_SCORE = 0, TWINKV_OP_SELECT = 1, TWINKV_OP_REPAIR = 2 };
 
 /* Phase counts for the `marks` argument. */
-enum { TWINKV_SCORE_PHASES = 2, TWINKV_SELECT_PHASES = 1, TWINKV_REPAIR_PHASES = 4, TWINKV_GATHER_PHASES = 1 };
+enum { TWINKV_SCORE_PHASES = 2, TWINKV_SELECT_PHASES = 1, TWINKV_REPAIR_PHASES = 4, TWINKV_GATHER_PHASES = 1,
+       TWINKV_ALLOC_PHASES = 3 };
 
 /* Bytes of workspace an operation needs for these parameters; 0 if the
  * parameters are invalid (see the entry points) or the op needs none. */
@@ -186,6 +190,39 @@ int twinkv_repair(const twinkv_params* params, const void* keys, const uint8_t* 
 int twinkv_gather_kv(const twinkv_params* params, const void* keys, const void* values, const int32_t* kept_idx,
                      const int64_t* kept_off, int64_t total, void* out_keys, void* out_values, hipStream_t stream,
                      hipEvent_t* marks);
+
+/*
+ * twinkv_allocate - per-head capacities from prefix attention ([P2] section
+ * 3.3, Equation 5; appendices A.2, A.3).  The G = L*H heads form L layers of
+ * H consecutive KV heads that share the per-head budget B (0 <= B <= N).
+ * For KV head g, its Gq query heads observe the prefix from the last W
+ * positions t = N-W .. N-1 (queries[g][q][w] is query head q at position
+ * N-W+w, post-RoPE):
+ *   a[q,w,i] = exp(q.k_i/sqrt(d)) / sum_{j<=t} exp(q.k_j/sqrt(d))  for i <= t, else 0
+ *   z[g][i]  = fp32( max over |i'-i| <= pool/2 of  (1/Gq) sum_q sum_w a[q,w,i'] )
+ * (logits and sums evaluated in fp64, bf16 products exact; the window is cut
+ * at the ends of the prefix).  With s = min(sink, B), r = min(recent, B-s),
+ * P = s + r and U = B - P, g_h counts head h's positions among the H*U
+ * largest unprotected z of its layer (ties to the lower head, then the lower
+ * position; a layer whose unprotected z are all zero gives g_h = U), and
+ *   capacity[h] = P + floor((g_h + U)/2) + delta_h,
+ * where the first R = H*U - sum floor((g_h+U)/2) heads of the layer with an
+ * odd g_h + U get delta_h = 1.  So every layer's capacities sum to H*B and
+ * each is at least P + floor(U/2).  U = 0 skips the allocation: capacity = B.
+ *   keys:     bf16 [G][N][d];  queries: bf16 [G][Gq][W][d]
+ *   capacity: int32 [G] (out);  g_count: int32 [G] (out, may be NULL; 0 when skipped)
+ *   z:        float [G][N] (out, may be NULL)
+ * Requirements (else TWINKV_ERR_ARG): 1 <= H <= 1024 dividing G, Gq >= 1,
+ * 1 <= W <= N, Gq*W <= 128, pool odd, H*N <= 2^30.  Of the parameters G, N,
+ * d, sink and recent are read.  Workspace: twinkv_allocate_workspace_bytes().
+ * Phases for `marks`: 0 = per-query softmax statistics, 1 = attention
+ * aggregation and pooling, 2 = layer-wide ranking and Equation 5.
+ */
+size_t twinkv_allocate_workspace_bytes(const twinkv_params* params, int32_t H, int32_t Gq, int32_t W, int32_t pool,
+                                       int64_t B);
+int twinkv_allocate(const twinkv_params* params, int32_t H, int32_t Gq, int32_t W, int32_t pool, int64_t B,
+                    const void* keys, const void* queries, int32_t* capacity, int32_t* g_count, float* z,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* marks);
 
 #ifdef __cplusplus
 }

@@ -1,10 +1,11 @@
 """MI355X (gfx950) key-redundancy scoring: TwinKV's nonlocal key-similarity
 count, best twin, value-energy score, exact-budget selection,
-orphan/donor repair and the packed cache of the retained keys and values,
-computed by hand-written HIP kernels behind a C ABI
+orphan/donor repair, the packed cache of the retained keys and values and
+per-head capacities from prefix attention, computed by hand-written HIP kernels behind a C ABI
 (include/twinkv.h).  This package is the thin Python binding."""
 from ._lib import (  # noqa: F401
     Events,
+    allocate,
     Params,
     TwinKVError,
     capacity_offsets,

@@ -21,7 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "twinkv.h")
 
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 OP_SCORE, OP_SELECT, OP_REPAIR = 0, 1, 2
-SCORE_PHASES, SELECT_PHASES, REPAIR_PHASES, GATHER_PHASES = 2, 1, 4, 1
+SCORE_PHASES, SELECT_PHASES, REPAIR_PHASES, GATHER_PHASES, ALLOC_PHASES = 2, 1, 4, 1, 3
 
 
 class Params(ctypes.Structure):
@@ -70,6 +70,11 @@ def load():
     lib.twinkv_repair.restype = ctypes.c_int
     lib.twinkv_gather_kv.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp, vp]
     lib.twinkv_gather_kv.restype = ctypes.c_int
+    i32 = ctypes.c_int32
+    lib.twinkv_allocate_workspace_bytes.argtypes = [P, i32, i32, i32, i32, i64]
+    lib.twinkv_allocate_workspace_bytes.restype = sz
+    lib.twinkv_allocate.argtypes = [P, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    lib.twinkv_allocate.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -337,3 +342,38 @@ def gather_kv(keys, values, kept_idx, offsets, out=None, events=None, total=None
                               _stream(), _marks(events, GATHER_PHASES))
     _check(st, "twinkv_gather_kv")
     return {"keys": ok, "values": ov, "offsets": off_dev, "total": total}
+
+
+def allocate(keys, queries, heads_per_layer, budget, sink=4, recent=64, pool=7, out=None, ws=None, events=None):
+    """Per-head capacities of every layer from prefix attention (Equation 5).
+
+    keys: bf16 [G][N][d]; queries: bf16 [G][Gq][W][d], the post-RoPE queries of
+    the last W prefix positions of the Gq query heads sharing each KV head.
+    Consecutive groups of ``heads_per_layer`` heads share the per-head
+    ``budget``.  Returns capacity (int32 [G]), g_count (int32 [G]) and the
+    pooled scores z (float32 [G][N]) as device tensors, plus the workspace."""
+    lib = load()
+    keys = _as_bf16_bits(keys, "keys")
+    G, N, d = keys.shape
+    dev = keys.device
+    if queries.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not queries.is_cuda \
+            or not queries.is_contiguous() or queries.dim() != 4 or queries.shape[0] != G or queries.shape[3] != d:
+        raise ValueError("queries must be a contiguous bf16 device tensor [G][Gq][W][d]")
+    Gq, W = int(queries.shape[1]), int(queries.shape[2])
+    H = int(heads_per_layer)
+    p = params(G, N, d, 0.0, 0, sink, recent)
+    out = {} if out is None else out
+    o = {
+        "capacity": _need(out.get("capacity"), (G,), torch.int32, dev, "capacity"),
+        "g_count": _need(out.get("g_count"), (G,), torch.int32, dev, "g_count"),
+        "z": _need(out.get("z"), (G, N), torch.float32, dev, "z"),
+    }
+    nb = int(lib.twinkv_allocate_workspace_bytes(ctypes.byref(p), H, Gq, W, int(pool), int(budget)))
+    ws = _workspace(ws, nb, dev)
+    wp, wn = _ws_ptr(ws)
+    st = lib.twinkv_allocate(ctypes.byref(p), H, Gq, W, int(pool), int(budget), _ptr(keys), _ptr(queries),
+                             _ptr(o["capacity"]), _ptr(o["g_count"]), _ptr(o["z"]), wp, wn, _stream(),
+                             _marks(events, ALLOC_PHASES))
+    _check(st, "twinkv_allocate")
+    o["ws"] = ws
+    return o

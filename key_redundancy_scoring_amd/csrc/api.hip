@@ -59,6 +59,44 @@ size_t repair_ws(const twinkv_params* p) {
          align_up(n * (size_t)p->d * sizeof(uint16_t)) + align_up(n * sizeof(float));
 }
 
+struct AllocShape {
+  int64_t Q, nchunk, width, s_cnt, r_cnt, P, U, L;
+};
+
+AllocShape alloc_shape(const twinkv_params* p, int32_t H, int32_t Gq, int32_t W, int64_t B) {
+  AllocShape a{};
+  a.Q = (int64_t)Gq * W;
+  a.nchunk = (p->N + 255) / 256;
+  a.s_cnt = p->sink < B ? p->sink : B;
+  a.r_cnt = p->recent < B - a.s_cnt ? p->recent : B - a.s_cnt;
+  a.P = a.s_cnt + a.r_cnt;
+  a.U = B - a.P;
+  a.width = p->N - a.P;
+  a.L = p->G / H;
+  return a;
+}
+
+int check_alloc(const twinkv_params* p, int32_t H, int32_t Gq, int32_t W, int32_t pool, int64_t B) {
+  const int rc = check_sizes(p);
+  if (rc != TWINKV_OK) return rc;
+  if (p->d != 64 && p->d != 128) return TWINKV_ERR_UNSUPPORTED;
+  if (H < 1 || H > kMaxHeads || p->G % H != 0) return TWINKV_ERR_ARG;
+  if (Gq < 1 || W < 1 || W > p->N || (int64_t)Gq * W > kMaxQueries) return TWINKV_ERR_ARG;
+  if (pool < 1 || (pool & 1) == 0) return TWINKV_ERR_ARG;
+  if (B < 0 || B > p->N) return TWINKV_ERR_ARG;
+  if ((int64_t)H * p->N > (int64_t(1) << 30)) return TWINKV_ERR_ARG;
+  return TWINKV_OK;
+}
+
+size_t alloc_ws(const twinkv_params* p, int32_t H, int32_t Gq, int32_t W, int64_t B) {
+  const AllocShape s = alloc_shape(p, H, Gq, W, B);
+  const size_t G = (size_t)p->G, N = (size_t)p->N;
+  return align_up(G * s.nchunk * s.Q * 2 * sizeof(double)) + align_up(G * s.Q * 2 * sizeof(double)) +
+         align_up(G * N * sizeof(double)) + align_up(G * N * sizeof(float)) +
+         align_up(G * (size_t)s.width * sizeof(double)) + align_up(G * (size_t)s.width) +
+         align_up((size_t)s.L * sizeof(int32_t));
+}
+
 int record(hipEvent_t* marks, int k, hipStream_t s) {
   if (!marks) return TWINKV_OK;
   return hipEventRecord(marks[k], s) == hipSuccess ? TWINKV_OK : TWINKV_ERR_HIP;
@@ -185,6 +223,83 @@ int twinkv_gather_kv(const twinkv_params* p, const void* keys, const void* value
                            kept_off, p->G, p->N, p->d, total, static_cast<uint16_t*>(out_keys),
                            static_cast<uint16_t*>(out_values), stream));
   TRY(record(marks, 1, stream));
+  return TWINKV_OK;
+}
+
+size_t twinkv_allocate_workspace_bytes(const twinkv_params* p, int32_t H, int32_t Gq, int32_t W, int32_t pool,
+                                       int64_t B) {
+  return check_alloc(p, H, Gq, W, pool, B) == TWINKV_OK ? alloc_ws(p, H, Gq, W, B) : 0;
+}
+
+int twinkv_allocate(const twinkv_params* p, int32_t H, int32_t Gq, int32_t W, int32_t pool, int64_t B,
+                    const void* keys, const void* queries, int32_t* capacity, int32_t* g_count, float* z,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* marks) {
+  TRY(check_alloc(p, H, Gq, W, pool, B));
+  if (!keys || !queries || !capacity) return TWINKV_ERR_ARG;
+  if (!aligned16(keys) || !aligned16(queries)) return TWINKV_ERR_ARG;
+  const size_t need = alloc_ws(p, H, Gq, W, B);
+  if (!workspace || workspace_bytes < need) return TWINKV_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return TWINKV_ERR_ARG;
+  const AllocShape sh = alloc_shape(p, H, Gq, W, B);
+  const size_t G = (size_t)p->G, N = (size_t)p->N;
+  Carve cv{static_cast<char*>(workspace)};
+  AttnArgs aa{};
+  aa.part = cv.take<double>(G * sh.nchunk * sh.Q * 2);
+  aa.mz = cv.take<double>(G * sh.Q * 2);
+  aa.agg = cv.take<double>(G * N);
+  float* zbuf = cv.take<float>(G * N);
+  aa.pool_score = cv.take<double>(G * (size_t)sh.width);
+  uint8_t* pool_keep = cv.take<uint8_t>(G * (size_t)sh.width);
+  int32_t* pool_cap = cv.take<int32_t>((size_t)sh.L);
+  aa.keys = static_cast<const uint16_t*>(keys);
+  aa.queries = static_cast<const uint16_t*>(queries);
+  aa.G = p->G;
+  aa.N = p->N;
+  aa.Gq = Gq;
+  aa.W = W;
+  aa.pool = pool;
+  aa.nchunk = sh.nchunk;
+  aa.inv_sqrt_d = 1.0 / sqrt((double)p->d);
+  aa.inv_gq = 1.0 / (double)Gq;
+  aa.z = z ? z : zbuf;
+  aa.s_cnt = sh.s_cnt;
+  aa.r_cnt = sh.r_cnt;
+
+  TRY(record(marks, 0, stream));
+  TRY_HIP(launch_attn(aa, p->d, 1, stream));
+  TRY(record(marks, 1, stream));
+  TRY_HIP(launch_attn(aa, p->d, 2, stream));
+  TRY(record(marks, 2, stream));
+  if (sh.U == 0) {
+    // no unprotected slots: allocation is skipped and every head keeps B
+    TRY_HIP(launch_fill_capacity(capacity, g_count, p->G, (int32_t)B, stream));
+  } else {
+    TRY_HIP(launch_fill_capacity(pool_cap, nullptr, sh.L, (int32_t)(H * sh.U), stream));
+    SelectArgs sa{};
+    sa.score = aa.pool_score;
+    sa.energy = aa.pool_score;  // equal scores fall through to the pool index: head, then position
+    sa.capacity = pool_cap;
+    sa.keep = pool_keep;
+    sa.kept_idx = nullptr;
+    sa.kept_idx_len = 0;
+    sa.G = sh.L;
+    sa.N = (int64_t)H * sh.width;
+    sa.sink = 0;
+    sa.recent = 0;
+    TRY_HIP(launch_select(sa, stream));
+    AllocArgs al{};
+    al.L = sh.L;
+    al.H = H;
+    al.width = sh.width;
+    al.U = sh.U;
+    al.P = sh.P;
+    al.pool_keep = pool_keep;
+    al.pool_score = aa.pool_score;
+    al.capacity = capacity;
+    al.g_count = g_count;
+    TRY_HIP(launch_alloc(al, stream));
+  }
+  TRY(record(marks, 3, stream));
   return TWINKV_OK;
 }
 

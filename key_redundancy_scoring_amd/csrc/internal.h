@@ -61,6 +61,38 @@ hipError_t launch_gather_kv(const uint16_t* keys, const uint16_t* values, const 
                             const int64_t* kept_off, int64_t G, int64_t N, int d, int64_t total, uint16_t* out_keys,
                             uint16_t* out_values, hipStream_t stream);
 
+// Head allocation from prefix attention (alloc.hip).
+constexpr int kMaxQueries = 128;  // Gq * W observing queries per KV head
+constexpr int kMaxHeads = 1024;   // KV heads per layer
+
+struct AttnArgs {
+  const uint16_t* keys;     // bf16 [G][N][d]
+  const uint16_t* queries;  // bf16 [G][Gq][W][d]
+  int64_t G, N;
+  int32_t Gq, W, pool;
+  int64_t nchunk;           // blocks of 256 keys per head
+  double inv_sqrt_d, inv_gq;
+  double* part;             // [G][nchunk][Gq*W][2] block (max, sum of exp)
+  double* mz;               // [G][Gq*W][2] per query (max, normaliser)
+  double* agg;              // [G][N] attention summed over queries, averaged over query heads
+  float* z;                 // [G][N] pooled fp32 scores
+  double* pool_score;       // [G][N - s - r] unprotected scores, head after head
+  int64_t s_cnt, r_cnt;     // protected leading / trailing positions
+};
+struct AllocArgs {
+  int64_t L;                // layers
+  int32_t H;                // KV heads per layer
+  int64_t width;            // unprotected positions per head
+  int64_t U, P;
+  const uint8_t* pool_keep; // [L][H * width] selected pool entries
+  const double* pool_score; // [L][H * width]
+  int32_t* capacity;        // [G] out
+  int32_t* g_count;         // [G] out, may be null
+};
+hipError_t launch_attn(const AttnArgs& a, int d, int phase, hipStream_t stream);
+hipError_t launch_alloc(const AllocArgs& a, hipStream_t stream);
+hipError_t launch_fill_capacity(int32_t* capacity, int32_t* g_count, int64_t G, int32_t B, hipStream_t stream);
+
 struct SwapArgs {
   const uint8_t* keep_in;
   const double* best;

@@ -15,8 +15,10 @@ Sources (cited by page title and section / equation; no line numbers):
 * [P2] "Small Frequency Corrections Can Change What Survives KV Cache
   Compression" (paperpeel page): section 3.1 exact budget and protected
   positions, section 3.2 value-weighted nonlocal key rarity (count, value
-  energy, discounted score, tie rule), section 3.4 selection in sequence order
-  and the packed, unpadded cache layout,
+  energy, discounted score, tie rule), section 3.3 head allocation from prefix
+  attention (Equation 5), section 3.4 selection in sequence order and the
+  packed, unpadded cache layout, appendix A.2 prefix-attention statistics,
+  appendix A.3 budget conservation,
   appendix A.1 boundary handling and the Figure 3 example.
 
 Every quantity is evaluated straight from its definition in float64.  Keys and
@@ -38,7 +40,15 @@ design notes of the repository as well):
   recent = min(recent, b - s) (P2 section 3.1 and appendix A.1 applied per head);
 * repair protects the same clipped regions computed with K = |S0|; protected
   positions that S0 evicted may still be orphans; only donors exclude them;
-* all ties go to the lowest position.
+* all ties go to the lowest position;
+* head allocation (P2 section 3.3, A.2): the W = 32 queries are those of the
+  last W prefix positions; the attention of the Gq query heads sharing a KV
+  head is averaged and that of the W queries summed (a sum and a mean differ
+  by W = 32, a power of two, so no float32 score or ranking changes); the
+  max-pool window of 7 is centred and cut at the ends of the prefix, and
+  pooling comes before protected positions are excluded; the scores are
+  evaluated in float64 and rounded once to float32, the precision the page
+  names, and the global ranking compares those float32 values.
 """
 from __future__ import annotations
 
@@ -286,6 +296,77 @@ def repair_head(K: np.ndarray, retained: np.ndarray, tau: float, window: int, si
         "m": int(m),
         "pairs": pairs.astype(np.int64),
     }
+
+
+# ----------------------------------------------------------------------------
+# [P2] section 3.3 and appendix A.2: head capacities from prefix attention
+
+
+def prefix_attention_scores(K: np.ndarray, Q: np.ndarray, pool: int = 7) -> np.ndarray:
+    """Capacity statistics of one KV head ([P2] section 3.3, appendix A.2).
+
+    ``K``: the head's keys [N][d]; ``Q``: the queries of its Gq query heads at
+    the last W prefix positions t = N-W .. N-1, [Gq][W][d] (all float64).
+    a[g,t,i] = exp(q_{g,t}.k_i / sqrt(d)) / sum_{j<=t} exp(q_{g,t}.k_j / sqrt(d))
+    for i <= t and 0 for i > t (the causal softmax of A.2).  The Gq query
+    heads are averaged, the W queries summed, and the result max-pooled over
+    positions with a centred window of ``pool`` positions cut at the ends of
+    the prefix.  Returns the pooled score of every position (float64)."""
+    K = np.asarray(K, dtype=np.float64)
+    Q = np.asarray(Q, dtype=np.float64)
+    N, d = K.shape
+    Gq, W, _ = Q.shape
+    t_pos = np.arange(N - W, N)
+    logits = np.einsum("gtd,nd->gtn", Q, K) / math.sqrt(d)
+    causal = np.arange(N)[None, None, :] <= t_pos[None, :, None]
+    logits = np.where(causal, logits, -np.inf)
+    m = logits.max(axis=2, keepdims=True)
+    ex = np.where(causal, np.exp(logits - m), 0.0)
+    a = ex / ex.sum(axis=2, keepdims=True)
+    agg = a.mean(axis=0).sum(axis=0)
+    half = pool // 2
+    z = np.empty(N)
+    for i in range(N):
+        z[i] = agg[max(0, i - half):min(N, i + half + 1)].max()
+    return z
+
+
+def allocate_heads(z: np.ndarray, N: int, B: int, sink: int, recent: int) -> dict:
+    """Equation 5 of [P2] section 3.3 for one layer's H KV heads sharing the
+    per-head budget B ([P2] appendices A.2, A.3).
+
+    ``z``: float32 [H][N] capacity scores.  With s = min(sink, B), w =
+    min(recent, B - s), P = s + w, U = B - P: g_h counts head h's positions
+    among the H*U largest unprotected scores of the layer (ties to the lower
+    head, then the lower position; all scores zero gives g_h = U);
+    u~_h = (g_h + U)/2, u_h = floor(u~_h) + delta_h where the first
+    R = H*U - sum floor(u~_h) heads with fractional part 1/2 get delta = 1;
+    b_h = P + u_h.  U = 0 skips the allocation (b_h = B)."""
+    z = np.asarray(z, dtype=np.float32)
+    H = z.shape[0]
+    s_cnt, r_cnt = protected_counts(B, sink, recent)
+    P = s_cnt + r_cnt
+    U = B - P
+    if U == 0:
+        return {"b": np.full(H, B, np.int64), "g": np.zeros(H, np.int64), "P": P, "U": U}
+    lo, hi = s_cnt, N - r_cnt
+    vals = z[:, lo:hi].astype(np.float64)
+    if not np.any(vals != 0.0):
+        g = np.full(H, U, np.int64)
+    else:
+        flat = vals.reshape(-1)
+        order = np.lexsort((np.arange(flat.size), -flat))  # score desc, then head, then position
+        pick = order[:H * U]
+        g = np.bincount(pick // vals.shape[1], minlength=H).astype(np.int64)
+    twice = g + U                       # 2 * u~_h, an integer
+    fl = twice // 2
+    R = H * U - int(fl.sum())
+    half = np.flatnonzero(twice % 2 == 1)
+    delta = np.zeros(H, np.int64)
+    delta[half[:R]] = 1
+    b = P + fl + delta
+    assert int(b.sum()) == H * B
+    return {"b": b, "g": g, "P": P, "U": U}
 
 
 # ----------------------------------------------------------------------------

@@ -1,7 +1,8 @@
 """Seeded synthetic inputs shared by the oracle-side tests and the GPU path.
 
 This package builds inputs only: post-RoPE keys with planted near-duplicate
-clusters, value vectors, per-head capacities and random retained sets.  It
+clusters, value vectors, post-RoPE queries of the last prefix positions,
+per-head capacities and random retained sets.  It
 holds none of the scoring, selection or repair arithmetic; both the oracle
 and the HIP library consume what it produces.
 """
@@ -13,6 +14,7 @@ from .generator import (
     gumbel_retained,
     make_head,
     make_heads,
+    make_queries,
     rope_tables,
 )
 
@@ -26,5 +28,6 @@ __all__ = [
     "gumbel_retained",
     "make_head",
     "make_heads",
+    "make_queries",
     "rope_tables",
 ]

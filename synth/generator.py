@@ -36,6 +36,7 @@ from .configs import Config
 # Offsets that keep the auxiliary streams apart from the per-head key streams.
 _CAPACITY_STREAM = 1_000_003
 _GUMBEL_STREAM = 2
+_QUERY_STREAM = 3
 
 
 def _head_rng(cfg: Config, g: int, *extra: int) -> np.random.Generator:
@@ -283,3 +284,28 @@ def gumbel_retained(cfg: Config, g: int, N: int | None = None, keep: int | None 
     m = np.zeros(N, dtype=np.uint8)
     m[idx] = 1
     return m
+
+
+def make_queries(cfg: Config, g: int, Gq: int = 4, W: int = 32, N: int | None = None, d: int | None = None):
+    """Post-RoPE queries of the last W prefix positions for the Gq query heads
+    that share KV head ``g`` ([Gq][W][d] bf16 bits).
+
+    Raw queries are N(0, s_g^2) with one sharpness s_g per KV head, drawn
+    log-uniformly from [0.25, 2]: heads differ in how concentrated their
+    attention over the prefix is, which is what capacity allocation reacts
+    to.  Query t is rotated with the workload's base at position N - W + t.
+    """
+    N = cfg.N if N is None else int(N)
+    d = cfg.d if d is None else int(d)
+    W = min(int(W), N)
+    rng = _head_rng(cfg, g, _QUERY_STREAM)
+    s_g = float(np.exp(rng.uniform(np.log(0.25), np.log(2.0))))
+    X = rng.standard_normal((Gq, W, d), dtype=np.float32).astype(np.float64) * s_g
+    cos, sin = rope_tables(N, d, cfg.rope_base)
+    cos, sin = cos[N - W:], sin[N - W:]
+    half = d // 2
+    a, b = X[..., :half], X[..., half:]
+    out = np.empty_like(X)
+    out[..., :half] = a * cos - b * sin
+    out[..., half:] = a * sin + b * cos
+    return f64_to_bf16_bits(out)

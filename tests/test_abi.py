@@ -16,8 +16,9 @@ FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: every call belo
 def test_library_exports_every_header_symbol():
     lib = krs.load()
     declared = krs.header_symbols()
-    assert declared == ["twinkv_gather_kv", "twinkv_repair", "twinkv_score", "twinkv_select",
-                        "twinkv_status_string", "twinkv_uniform_capacity", "twinkv_workspace_bytes"]
+    assert declared == ["twinkv_allocate", "twinkv_allocate_workspace_bytes", "twinkv_gather_kv", "twinkv_repair",
+                        "twinkv_score", "twinkv_select", "twinkv_status_string", "twinkv_uniform_capacity",
+                        "twinkv_workspace_bytes"]
     for name in declared:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
@@ -127,3 +128,26 @@ def test_gather_validation():
     ]
     for pp, k, v, idx, off, total, ok_, ov, want in bad:
         assert lib.twinkv_gather_kv(ctypes.byref(pp), k, v, idx, off, total, ok_, ov, None, None) == want
+
+
+def test_allocate_validation():
+    lib = krs.load()
+    p = L.params(16, 1000, 64, 0.0, 0, 4, 64)
+    nb = lib.twinkv_allocate_workspace_bytes(ctypes.byref(p), 8, 4, 32, 7, 500)
+    assert nb > 16 * 1000 * (8 + 4 + 8)  # agg, z and pool at least
+    bad_shapes = [(3, 4, 32, 7, 500),     # H does not divide G
+                  (8, 4, 33, 7, 500),     # Gq * W above 128
+                  (8, 4, 0, 7, 500),      # no queries
+                  (8, 4, 32, 6, 500),     # even pool
+                  (8, 4, 32, 7, 1001),    # budget above N
+                  (8, 4, 32, 7, -1)]
+    for H, Gq, W, pool, B in bad_shapes:
+        assert lib.twinkv_allocate_workspace_bytes(ctypes.byref(p), H, Gq, W, pool, B) == 0
+        assert lib.twinkv_allocate(ctypes.byref(p), H, Gq, W, pool, B, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40,
+                                   None, None) == L.ERR_ARG
+    assert lib.twinkv_allocate(ctypes.byref(L.params(16, 1000, 32, 0.0, 0)), 8, 4, 32, 7, 500, FAKE, FAKE, FAKE, None,
+                               None, FAKE, 1 << 40, None, None) == L.ERR_UNSUPPORTED
+    assert lib.twinkv_allocate(ctypes.byref(p), 8, 4, 32, 7, 500, FAKE, FAKE, None, None, None, FAKE, 1 << 40, None,
+                               None) == L.ERR_ARG  # no capacity output
+    assert lib.twinkv_allocate(ctypes.byref(p), 8, 4, 32, 7, 500, FAKE, FAKE, FAKE, None, None, FAKE, nb - 1, None,
+                               None) == L.ERR_WORKSPACE

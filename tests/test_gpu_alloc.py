@@ -1,0 +1,121 @@
+"""GPU parity of the head allocation (twinkv_allocate) against the oracle's
+prefix_attention_scores and allocate_heads, on seeded synthetic keys and
+queries: the pooled fp32 scores of every position and the integer
+capacities and layer counts of every head, at sizes that span several key
+blocks and a ragged tail, both head dims, the short-prefix case where the
+allocation is skipped, and the full 32k workload (all 16 layers launched,
+the first and last checked against the oracle, every layer by its budget
+properties).
+"""
+import numpy as np
+import pytest
+import torch
+
+import key_redundancy_scoring_amd as krs
+from oracle import twinkv_oracle as O
+from synth import get_config, make_heads, make_queries
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _up(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(_dev())
+
+
+def _inputs(cfg, G, N, Gq=4, W=32):
+    K, _, _ = make_heads(cfg, heads=range(G), N=N, with_values=False)
+    Q = np.stack([make_queries(cfg, g, Gq=Gq, W=W, N=N) for g in range(G)])
+    return K, Q
+
+
+def _oracle_layer(K, Q, heads, N, B, sink, recent, pool=7):
+    z = np.stack([O.prefix_attention_scores(O.widen_bf16(K[g]), O.widen_bf16(Q[g]), pool) for g in heads])
+    z32 = z.astype(np.float32)
+    return z32, O.allocate_heads(z32, N, B, sink, recent)
+
+
+def _check_layers(K, Q, res, H, N, B, sink, recent, layers, tag):
+    z_gpu = res["z"].cpu().numpy()
+    cap = res["capacity"].cpu().numpy()
+    gc = res["g_count"].cpu().numpy()
+    for layer in layers:
+        heads = range(layer * H, (layer + 1) * H)
+        z_ref, ref = _oracle_layer(K, Q, heads, N, B, sink, recent)
+        zg = z_gpu[layer * H:(layer + 1) * H]
+        # the same fp64 value rounded once to fp32 on both sides: equal unless
+        # a value sits within fp64 rounding of an fp32 rounding boundary
+        diff = zg != z_ref
+        assert diff.mean() < 1e-5, f"{tag} layer {layer}: {diff.sum()} pooled scores differ"
+        np.testing.assert_allclose(zg, z_ref, rtol=2.0 ** -23, atol=0, err_msg=f"{tag} layer {layer} z")
+        if not diff.any():
+            np.testing.assert_array_equal(cap[layer * H:(layer + 1) * H], ref["b"], err_msg=f"{tag} layer {layer} b")
+            if ref["U"] > 0:
+                np.testing.assert_array_equal(gc[layer * H:(layer + 1) * H], ref["g"], err_msg=f"{tag} layer {layer} g")
+        _say(f"[{tag}] layer {layer}: b = {cap[layer * H:(layer + 1) * H].tolist()}")
+
+
+def _check_budget(res, H, B, P, U, tag):
+    cap = res["capacity"].cpu().numpy().reshape(-1, H)
+    assert np.all(cap.sum(1) == H * B), f"{tag} layer budgets"
+    assert np.all(cap >= P + U // 2), f"{tag} capacity floor"
+
+
+@pytest.mark.parametrize("cfg_id,L,H,N", [(2, 2, 8, 1500), (3, 1, 8, 700), (2, 1, 4, 300)])
+def test_allocation_small(cfg_id, L, H, N):
+    cfg = get_config(cfg_id)
+    G = L * H
+    K, Q = _inputs(cfg, G, N)
+    B = O.uniform_budget(N, 0.5)
+    res = krs.allocate(_up(K), _up(Q), H, B, cfg.sink, cfg.recent)
+    torch.cuda.synchronize()
+    _check_layers(K, Q, res, H, N, B, cfg.sink, cfg.recent, range(L), f"cfg{cfg_id} N{N}")
+    s, r = O.protected_counts(B, cfg.sink, cfg.recent)
+    _check_budget(res, H, B, s + r, B - s - r, "small")
+
+
+def test_allocation_short_prefix_skipped():
+    """N = 172 at r = 0.75: the 43-slot budget is all protection, U = 0."""
+    cfg = get_config(2)
+    N, H = 172, 8
+    K, Q = _inputs(cfg, H, N)
+    B = O.uniform_budget(N, 0.75)
+    res = krs.allocate(_up(K), _up(Q), H, B, cfg.sink, cfg.recent)
+    torch.cuda.synchronize()
+    assert res["capacity"].cpu().numpy().tolist() == [B] * H
+    _check_layers(K, Q, res, H, N, B, cfg.sink, cfg.recent, [0], "short prefix")
+
+
+def test_allocation_few_queries_and_budget_extremes():
+    cfg = get_config(2)
+    N, H = 200, 4
+    K, Q = _inputs(cfg, H, N, Gq=2, W=5)
+    for B in (0, 1, 69, 150, N):
+        res = krs.allocate(_up(K), _up(Q), H, B, cfg.sink, cfg.recent, pool=3)
+        torch.cuda.synchronize()
+        cap = res["capacity"].cpu().numpy()
+        z_ref = np.stack([O.prefix_attention_scores(O.widen_bf16(K[g]), O.widen_bf16(Q[g]), 3) for g in range(H)])
+        ref = O.allocate_heads(z_ref.astype(np.float32), N, B, cfg.sink, cfg.recent)
+        np.testing.assert_array_equal(cap, ref["b"], err_msg=f"B={B}")
+
+
+def test_allocation_fullsize_llama32_1b_32k():
+    cfg = get_config(2)
+    H = 8
+    G, N = cfg.G, cfg.N
+    _say(f"[alloc 32k] generating G={G} N={N}")
+    K, Q = _inputs(cfg, G, N)
+    B = O.uniform_budget(N, cfg.removal)
+    res = krs.allocate(_up(K), _up(Q), H, B, cfg.sink, cfg.recent)
+    torch.cuda.synchronize()
+    s, r = O.protected_counts(B, cfg.sink, cfg.recent)
+    _check_budget(res, H, B, s + r, B - s - r, "alloc 32k")
+    _check_layers(K, Q, res, H, N, B, cfg.sink, cfg.recent, [0, G // H - 1], "alloc 32k")

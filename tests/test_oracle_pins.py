@@ -475,3 +475,111 @@ def test_pack_retained_rejects_unordered_and_handles_empty():
         O.pack_retained(K, None, [[2, 1], []])
     Kp, Vp, off = O.pack_retained(K, None, [[], []])
     assert Kp.shape == (0, 8) and Vp is None and off.tolist() == [0, 0, 0]
+
+
+# ---------------------------------------------------------------------------
+# head allocation (section 3.3 and appendices A.1-A.3 of the frequency-correction page)
+
+
+def _layer_scores(H, N, lo, hi, high_counts):
+    """Scores 2.0 on the first high_counts[h] unprotected positions of head h, 1.0 elsewhere."""
+    z = np.ones((H, N), np.float32)
+    for h, c in enumerate(high_counts):
+        z[h, lo:lo + c] = 2.0
+    return z
+
+
+def test_allocation_two_head_example():
+    """A.1's constructed example: N = 512, r = 0.5 gives B = 256, P = 68,
+    U = 188; g = (80, 296) must give b = (202, 310)."""
+    g = _golden("budget_conservation.json")
+    N, B = g["N"], g["B"]
+    z = _layer_scores(2, N, 4, N - 64, [80, 296])
+    r = O.allocate_heads(z, N, B, 4, 64)
+    assert r["P"] == g["P"] and r["U"] == g["U"]
+    assert r["g"].tolist() == [80, 296]
+    assert r["b"].tolist() == g["capacities"]
+
+
+def test_allocation_conservation_and_floor_random():
+    rng = np.random.default_rng(11)
+    for trial in range(30):
+        H = int(rng.integers(1, 9))
+        N = int(rng.integers(80, 400))
+        B = int(rng.integers(0, N + 1))
+        z = rng.random((H, N)).astype(np.float32) ** 4
+        r = O.allocate_heads(z, N, B, 4, 64)
+        assert int(r["b"].sum()) == H * B
+        assert np.all(r["b"] >= r["P"] + r["U"] // 2)
+        assert np.all(r["b"] <= N)
+        if r["U"] > 0:
+            assert int(r["g"].sum()) == H * r["U"]
+
+
+def test_allocation_half_remainders_go_to_first_heads():
+    """U = 3, g = (2, 4): u~ = (2.5, 3.5), one slot of rounding goes to head 0."""
+    N, B = 40, 5  # sink 1, recent 1 -> P = 2, U = 3
+    z = _layer_scores(2, N, 1, N - 1, [2, 4])
+    r = O.allocate_heads(z, N, B, 1, 1)
+    assert r["g"].tolist() == [2, 4]
+    assert r["b"].tolist() == [2 + 3, 2 + 3]
+    z = _layer_scores(3, N, 1, N - 1, [2, 4, 3])  # u~ = (2.5, 3.5, 3): R = 1 -> head 0
+    r = O.allocate_heads(z, N, B, 1, 1)
+    assert r["g"].tolist() == [2, 4, 3] and r["b"].tolist() == [5, 5, 5]
+
+
+def test_allocation_ties_and_degenerate_cases():
+    N, B = 20, 10  # sink 1, recent 1 -> P = 2, U = 8, 18 unprotected per head
+    z = np.ones((2, N), np.float32)
+    r = O.allocate_heads(z, N, B, 1, 1)  # all equal: head 0's positions come first
+    assert r["g"].tolist() == [16, 0] and r["b"].tolist() == [2 + 12, 2 + 4]
+    z = np.zeros((3, N), np.float32)
+    z[:, 0] = 5.0  # only protected positions carry attention: the pool is all zero
+    r = O.allocate_heads(z, N, B, 1, 1)
+    assert r["g"].tolist() == [8, 8, 8] and r["b"].tolist() == [B, B, B]
+    sp = _golden("short_prefix_example.json")  # U = 0: allocation skipped
+    r = O.allocate_heads(np.random.default_rng(0).random((4, sp["N"])).astype(np.float32), sp["N"], sp["budget"],
+                         sp["sink_param"], sp["recent_param"])
+    assert r["U"] == 0 and r["b"].tolist() == [sp["budget"]] * 4
+
+
+def _attention_brute(K, Q, pool):
+    N, d = len(K), len(K[0])
+    Gq, W = len(Q), len(Q[0])
+    agg = [0.0] * N
+    for g in range(Gq):
+        for w in range(W):
+            t = N - W + w
+            logit = [math.fsum(Q[g][w][c] * K[j][c] for c in range(d)) / math.sqrt(d) for j in range(t + 1)]
+            m = max(logit)
+            den = math.fsum(math.exp(x - m) for x in logit)
+            for j in range(t + 1):
+                agg[j] += math.exp(logit[j] - m) / den / Gq
+    half = pool // 2
+    return [max(agg[max(0, i - half):min(N, i + half + 1)]) for i in range(N)]
+
+
+def test_prefix_attention_matches_brute_force():
+    rng = np.random.default_rng(4)
+    for N, d, Gq, W, pool in [(9, 4, 2, 3, 7), (12, 8, 4, 5, 3), (6, 4, 1, 6, 1)]:
+        K = rng.standard_normal((N, d)) * 2
+        Q = rng.standard_normal((Gq, W, d)) * 2
+        z = O.prefix_attention_scores(K, Q, pool)
+        ref = _attention_brute(K.tolist(), Q.tolist(), pool)
+        np.testing.assert_allclose(z, ref, rtol=1e-12, atol=0)
+
+
+def test_prefix_attention_closed_forms():
+    """Equal keys give the uniform causal softmax: query t puts 1/(t+1) on every
+    i <= t.  Without pooling the scores sum to W (each query's weights sum
+    to one); the width-7 pool takes the maximum of the 7 surrounding sums."""
+    N, d, Gq, W = 50, 8, 4, 32
+    K = np.ones((N, d))
+    Q = np.random.default_rng(2).standard_normal((Gq, W, d))
+    z1 = O.prefix_attention_scores(K, Q, pool=1)
+    t = np.arange(N - W, N)
+    expect = np.array([np.sum(1.0 / (t[t >= i] + 1)) for i in range(N)])
+    np.testing.assert_allclose(z1, expect, rtol=1e-13)
+    assert abs(z1.sum() - W) < 1e-12
+    z7 = O.prefix_attention_scores(K, Q, pool=7)
+    np.testing.assert_allclose(z7, [expect[max(0, i - 3):i + 4].max() for i in range(N)], rtol=1e-13)
