@@ -14,8 +14,8 @@ removal.
 
 Prints one JSON line.  `value` is keys (head positions) through the whole path
 per second.  `gather_kv` times, outside the step, the packed cache of the
-last step's selection (retained keys and values in sequence order), and
-`allocate` the per-head capacities from the attention of the last 32
+last step's selection (retained keys and values in sequence order),
+`variant_score` the keys of the permuted-count variant, and `allocate` the per-head capacities from the attention of the last 32
 synthetic prefix queries of each KV head (8 KV heads per layer).  `roofline` is for the dominant kernel, the score-mode Gram
 sweep, timed with HIP events that the library records around its launch on
 the stream it runs on; its `achieved` counts the algorithmic work, one
@@ -233,6 +233,22 @@ def main():
     gather_rows = gres["total"]
     gather_bytes = gather_rows * (8 * d + 4)
 
+    # score-variant keys (permuted counts, seed 11) for the last step's counts
+    from synth import count_permutation
+    permd = torch.from_numpy(np.stack([count_permutation(cfg, g, cap_list[g], 11) for g in range(G)])).to(dev)
+    vev = [krs.Events(2) for _ in range(args.steps)]
+    vout = {}
+    for k in range(args.steps + 1):
+        vres = krs.variant_score(s_out["count"], s_out["energy"], "twin", perm=permd, out=vout,
+                                 events=vev[k - 1] if k else None)
+        vout = vres
+    torch.cuda.synchronize()
+    variant_ms = float(np.mean([e.elapsed_ms(0, 1) for e in vev]))
+    for e in vev:
+        e.close()
+    variant_bytes = G * N * (4 + 8 + 4 + 4 + 16)  # perm, energy, own and permuted count, score and tie
+    del permd, vout, vres
+
     # per-head capacities from prefix attention, 8 KV heads per layer
     # (not part of the timed step)
     from synth import make_queries
@@ -301,6 +317,9 @@ def main():
         "gather_kv": {"ms": gather_ms, "rows": gather_rows, "algorithmic_bytes": gather_bytes,
                       "GBs": gather_bytes / (gather_ms * 1e-3) / 1e9,
                       "frac_hbm": gather_bytes / (gather_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "variant_score": {"ms": variant_ms, "variant": "twin with permuted counts (seed 11)",
+                          "GBs": variant_bytes / (variant_ms * 1e-3) / 1e9,
+                          "frac_hbm": variant_bytes / (variant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
         "allocate": {"ms": sum(alloc_ms), "stats_ms": alloc_ms[0], "aggregate_pool_ms": alloc_ms[1],
                      "rank_eq5_ms": alloc_ms[2], "heads_per_layer": Hkv, "queries_per_head": nq,
                      "logit_fp64_tflops": logit_flops / (alloc_ms[0] * 1e-3) / 1e12,

@@ -10,6 +10,8 @@
  *                  frequency-discounted score;
  *   twinkv_select  exact-budget per-head retention with protected sink and
  *                  recent positions;
+ *   twinkv_variant_score  selection keys of the score variants (value only,
+ *                  rarity only, permuted counts);
  *   twinkv_repair  the one-shot orphan/donor swap on a given retained set at
  *                  a fixed budget;
  *   twinkv_gather_kv  the packed, unpadded cache of the retained keys and
@@ -20,12 +22,13 @@
  * Sources (page title and section/equation):
  *   [P1] "TwinKV: A Composable Repair Pass for KV Cache Eviction via Pairwise
  *        Key Redundancy" (arXiv HTML): section 3.1, section 3.2 (Eq. 1, Eq. 2,
- *        protected regions), section 3.4 (Eq. 4, orphans, donors, swap).
+ *        Eq. 3, protected regions), section 3.4 (Eq. 4, orphans, donors, swap).
  *   [P2] "Small Frequency Corrections Can Change What Survives KV Cache
  *        Compression" (paperpeel): section 3.1 (budget, protection), section
  *        3.2 (count, energy, score, ties), section 3.3 (head allocation,
  *        Equation 5), section 3.4 (selection order and physical cache
- *        layout), appendices A.2, A.3 (prefix attention, budget proof).
+ *        layout), sections 5.3 and 5.5 (score ablations), appendices A.2,
+ *        A.3 (prefix attention, budget proof).
  *
  * Conventions for every entry point:
  *   - Array arguments are DEVICE pointers owned by the caller; the library
@@ -87,7 +90,10 @@ enum { TWINKV_OP_SCORE = 0, TWINKV_OP_SELECT = 1, TWINKV_OP_REPAIR = 2 };
 
 /* Phase counts for the `marks` argument. */
 enum { TWINKV_SCORE_PHASES = 2, TWINKV_SELECT_PHASES = 1, TWINKV_REPAIR_PHASES = 4, TWINKV_GATHER_PHASES = 1,
-       TWINKV_ALLOC_PHASES = 3 };
+       TWINKV_ALLOC_PHASES = 3, TWINKV_VARIANT_PHASES = 1 };
+
+/* Score variants for twinkv_variant_score. */
+enum { TWINKV_VARIANT_TWIN = 0, TWINKV_VARIANT_VALUE = 1, TWINKV_VARIANT_RARITY = 2 };
 
 /* Bytes of workspace an operation needs for these parameters; 0 if the
  * parameters are invalid (see the entry points) or the op needs none. */
@@ -96,6 +102,11 @@ size_t twinkv_workspace_bytes(int op, const twinkv_params* params);
 /* Uniform per-head capacity B = floor(N * (1 - removal)) ([P2] section 3.1,
  * "Equation 1").  Returns -1 if N < 0 or removal is outside [0, 1]. */
 int64_t twinkv_uniform_capacity(int64_t N, double removal);
+
+/* Capacity ceil(N * (1 - removal)) of [P1] section 3.1 (evaluated in
+ * double precision as written).  Returns -1 if N < 0 or removal is outside
+ * [0, 1]. */
+int64_t twinkv_uniform_capacity_ceil(int64_t N, double removal);
 
 /* Human-readable text for a twinkv_status value (static storage). */
 const char* twinkv_status_string(int status);
@@ -165,6 +176,30 @@ int twinkv_repair(const twinkv_params* params, const void* keys, const uint8_t* 
                   uint8_t* keep_out, double* best_sim, int32_t* best_idx, int32_t* n_orphans,
                   int32_t* n_donors, int32_t* n_swaps, int32_t* swap_pairs, void* workspace,
                   size_t workspace_bytes, hipStream_t stream, hipEvent_t* marks);
+
+/*
+ * twinkv_variant_score - selection keys of a score variant for twinkv_select,
+ * from the counts and energies twinkv_score wrote ([P1] section 3.2, Eq. 3;
+ * [P2] section 3.2 and the ablations of sections 5.3 and 5.5).  With
+ * c = count[g][perm[g][i]] (or count[g][i] when perm is NULL) and
+ * disc = ln((N+1)/(c+1)):
+ *   TWINKV_VARIANT_TWIN:   score = energy * disc,    tie = energy
+ *   TWINKV_VARIANT_VALUE:  score = energy,           tie = energy   (frequency removed)
+ *   TWINKV_VARIANT_RARITY: score = disc / ln(N+1),   tie = 0        (value removed: equal
+ *                          counts fall to the lower position; the order of [P1]'s -r/n)
+ * twinkv_select ranks by (score desc, tie desc, position asc), so passing
+ * score and tie as its score and energy arguments selects by the variant.
+ * The twin variant without perm reproduces twinkv_score's scores bit for bit;
+ * with perm it is [P2]'s permuted-frequency control (perm[g] a permutation of
+ * the head's unprotected positions, identity elsewhere; entries are clamped
+ * to [0, N)).  [P1]'s standalone score is the rarity variant with the
+ * capacity twinkv_uniform_capacity_ceil().
+ *   count: int32 [G][N] (>= 0); energy: double [G][N]; perm: int32 [G][N] or NULL
+ *   score, tie: double [G][N] (out; distinct from each other and from energy)
+ * Of the parameters only G and N are read.  Phases for `marks`: 0 = variant.
+ */
+int twinkv_variant_score(const twinkv_params* params, int variant, const int32_t* count, const double* energy,
+                         const int32_t* perm, double* score, double* tie, hipStream_t stream, hipEvent_t* marks);
 
 /*
  * twinkv_gather_kv - physical cache layout of a selection ([P2] section 3.4):

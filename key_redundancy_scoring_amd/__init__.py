@@ -18,5 +18,7 @@ from ._lib import (  # noqa: F401
     select,
     status_string,
     uniform_capacity,
+    uniform_capacity_ceil,
+    variant_score,
     workspace_bytes,
 )

@@ -21,7 +21,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "twinkv.h")
 
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 OP_SCORE, OP_SELECT, OP_REPAIR = 0, 1, 2
-SCORE_PHASES, SELECT_PHASES, REPAIR_PHASES, GATHER_PHASES, ALLOC_PHASES = 2, 1, 4, 1, 3
+SCORE_PHASES, SELECT_PHASES, REPAIR_PHASES, GATHER_PHASES, ALLOC_PHASES, VARIANT_PHASES = 2, 1, 4, 1, 3, 1
+VARIANTS = {"twin": 0, "value": 1, "rarity": 2}
 
 
 class Params(ctypes.Structure):
@@ -75,6 +76,10 @@ def load():
     lib.twinkv_allocate_workspace_bytes.restype = sz
     lib.twinkv_allocate.argtypes = [P, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.twinkv_allocate.restype = ctypes.c_int
+    lib.twinkv_uniform_capacity_ceil.argtypes = [i64, ctypes.c_double]
+    lib.twinkv_uniform_capacity_ceil.restype = i64
+    lib.twinkv_variant_score.argtypes = [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
+    lib.twinkv_variant_score.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -100,6 +105,10 @@ def workspace_bytes(op: int, p: Params) -> int:
 
 def uniform_capacity(N: int, removal: float) -> int:
     return int(load().twinkv_uniform_capacity(int(N), float(removal)))
+
+
+def uniform_capacity_ceil(N: int, removal: float) -> int:
+    return int(load().twinkv_uniform_capacity_ceil(int(N), float(removal)))
 
 
 def _ptr(t):
@@ -377,3 +386,30 @@ def allocate(keys, queries, heads_per_layer, budget, sink=4, recent=64, pool=7, 
     _check(st, "twinkv_allocate")
     o["ws"] = ws
     return o
+
+
+def variant_score(count_t, energy_t, variant, perm=None, out=None, events=None):
+    """Selection keys (score, tie) of a score variant ("twin", "value",
+    "rarity"), optionally with permuted counts (perm: int32 [G][N]); pass them
+    to select() as its score and energy."""
+    lib = load()
+    G, N = count_t.shape
+    dev = count_t.device
+    if count_t.dtype != torch.int32 or not count_t.is_contiguous() or not count_t.is_cuda:
+        raise ValueError("count must be a contiguous int32 device tensor [G][N]")
+    if energy_t.dtype != torch.float64 or tuple(energy_t.shape) != (G, N) or energy_t.device != dev \
+            or not energy_t.is_contiguous():
+        raise ValueError("energy must be a contiguous float64 [G][N] tensor on the counts' device")
+    if perm is not None and (perm.dtype != torch.int32 or tuple(perm.shape) != (G, N) or perm.device != dev
+                             or not perm.is_contiguous()):
+        raise ValueError("perm must be a contiguous int32 [G][N] tensor on the counts' device")
+    if variant not in VARIANTS:
+        raise ValueError(f"variant must be one of {sorted(VARIANTS)}")
+    out = {} if out is None else out
+    sc = _need(out.get("score"), (G, N), torch.float64, dev, "score")
+    tie = _need(out.get("tie"), (G, N), torch.float64, dev, "tie")
+    p = params(G, N, 0, 0.0, 0)
+    st = lib.twinkv_variant_score(ctypes.byref(p), VARIANTS[variant], _ptr(count_t), _ptr(energy_t), _ptr(perm),
+                                  _ptr(sc), _ptr(tie), _stream(), _marks(events, VARIANT_PHASES))
+    _check(st, "twinkv_variant_score")
+    return {"score": sc, "tie": tie}

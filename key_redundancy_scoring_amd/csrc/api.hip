@@ -132,6 +132,23 @@ int64_t twinkv_uniform_capacity(int64_t N, double removal) {
   return (int64_t)floor((double)N * (1.0 - removal));
 }
 
+int64_t twinkv_uniform_capacity_ceil(int64_t N, double removal) {
+  if (N < 0 || !(removal >= 0.0 && removal <= 1.0)) return -1;
+  return (int64_t)ceil((double)N * (1.0 - removal));
+}
+
+int twinkv_variant_score(const twinkv_params* p, int variant, const int32_t* count, const double* energy,
+                         const int32_t* perm, double* score, double* tie, hipStream_t stream, hipEvent_t* marks) {
+  TRY(check_sizes(p));
+  if (variant < TWINKV_VARIANT_TWIN || variant > TWINKV_VARIANT_RARITY) return TWINKV_ERR_ARG;
+  if (!count || !energy || !score || !tie) return TWINKV_ERR_ARG;
+  if (score == tie || score == energy || tie == energy) return TWINKV_ERR_ARG;
+  TRY(record(marks, 0, stream));
+  TRY_HIP(launch_variant(count, energy, perm, p->G, p->N, variant, score, tie, stream));
+  TRY(record(marks, 1, stream));
+  return TWINKV_OK;
+}
+
 size_t twinkv_workspace_bytes(int op, const twinkv_params* p) {
   switch (op) {
     case TWINKV_OP_SCORE: return check_params(p) == TWINKV_OK ? score_ws(p) : 0;

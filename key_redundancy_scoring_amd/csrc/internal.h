@@ -47,6 +47,10 @@ struct SelectArgs {
   int32_t sink, recent;
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+// Selection keys of a score variant (0 twin, 1 value, 2 rarity), optionally
+// with permuted counts.
+hipError_t launch_variant(const int32_t* count, const double* energy, const int32_t* perm, int64_t G, int64_t N,
+                          int variant, double* score, double* tie, hipStream_t stream);
 
 hipError_t launch_compact(const uint8_t* keep_in, int64_t G, int64_t N, int32_t* pos, int32_t* ncols,
                           hipStream_t stream);

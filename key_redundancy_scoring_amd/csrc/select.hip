@@ -111,7 +111,54 @@ __global__ __launch_bounds__(kBT) void select_kernel(SelectArgs a) {
   }
 }
 
+// Selection keys of the score variants (TwinKV page, section 3.2, Eq. 3;
+// frequency-correction page, sections 5.3 and 5.5): from the count c (of
+// position perm[i] when a permutation is given) and the energy e of each
+// position, with disc = ln((N+1)/(c+1)):
+//   twin:   score e * disc,           tie e
+//   value:  score e,                  tie e
+//   rarity: score disc / ln(N+1),     tie 0  (equal counts: lower position)
+// The expressions are the ones the score kernel evaluates, so the twin
+// variant without a permutation reproduces its scores bit for bit.
+__global__ __launch_bounds__(256) void variant_kernel(const int32_t* __restrict__ count,
+                                                     const double* __restrict__ energy,
+                                                     const int32_t* __restrict__ perm, int64_t G, int64_t N,
+                                                     int variant, double* __restrict__ score,
+                                                     double* __restrict__ tie) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= G * N) return;
+  int64_t src = i;
+  if (perm) {
+    int64_t p = perm[i];
+    p = p < 0 ? 0 : (p >= N ? N - 1 : p);
+    src = (i / N) * N + p;
+  }
+  const int c = count[src];
+  const double e = energy[i];
+  const double disc = log((double)(N + 1) / (double)(c + 1));
+  if (variant == 0) {
+    score[i] = e * disc;
+    tie[i] = e;
+  } else if (variant == 1) {
+    score[i] = e;
+    tie[i] = e;
+  } else {
+    score[i] = disc / log((double)(N + 1));
+    tie[i] = 0.0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_variant(const int32_t* count, const double* energy, const int32_t* perm, int64_t G, int64_t N,
+                          int variant, double* score, double* tie, hipStream_t stream) {
+  const int64_t n = G * N;
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(variant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, count, energy, perm, G, N, variant,
+                     score, tie);
+  return hipGetLastError();
+}
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.G), dim3(kBT), 0, stream, a);

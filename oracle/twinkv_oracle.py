@@ -231,6 +231,44 @@ def protected_mask(N: int, capacity: int, sink: int, recent: int) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# score variants: [P1] section 3.2 (Eq. 3) and the ablations of [P2]
+# sections 5.3 and 5.5
+
+
+def ceil_budget(N: int, removal: float) -> int:
+    """[P1] section 3.1: |S| = ceil((1 - rho) n), evaluated in float64."""
+    return int(math.ceil(N * (1.0 - removal)))
+
+
+def variant_scores(energy: np.ndarray, count: np.ndarray, N: int, variant: str, perm=None):
+    """Selection keys (score, tie) of one head for select_head, whose order is
+    (score desc, tie desc, position asc):
+
+    * "twin":   e * ln((N+1)/(c+1)), tie e ([P2] section 3.2);
+    * "value":  e, tie e (frequency removed, [P2] section 5.3);
+    * "rarity": the normalised discount ln((N+1)/(c+1)) / ln(N+1), tie 0, so
+      equal counts fall to the lower position (value removed, [P2] section
+      5.3); the same order as [P1]'s s = -r/n (Eq. 3), whose ties the page
+      leaves open (read: lower position first).
+
+    ``perm`` (optional, int [N]): position i takes the count of position
+    perm[i] (the within-head count permutation of [P2] section 5.5; the
+    caller permutes the unprotected positions among themselves)."""
+    e = np.asarray(energy, dtype=np.float64)
+    c = np.asarray(count, dtype=np.int64)
+    if perm is not None:
+        c = c[np.asarray(perm, dtype=np.int64)]
+    score, omega = frequency_score(e, c, N)
+    if variant == "twin":
+        return score, e
+    if variant == "value":
+        return e.copy(), e
+    if variant == "rarity":
+        return omega, np.zeros_like(e)
+    raise ValueError(variant)
+
+
+# ----------------------------------------------------------------------------
 # [P2] section 3.4: per-head selection
 
 

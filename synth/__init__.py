@@ -2,13 +2,14 @@
 
 This package builds inputs only: post-RoPE keys with planted near-duplicate
 clusters, value vectors, post-RoPE queries of the last prefix positions,
-per-head capacities and random retained sets.  It
+per-head capacities, random retained sets and count permutations.  It
 holds none of the scoring, selection or repair arithmetic; both the oracle
 and the HIP library consume what it produces.
 """
 from .configs import CONFIGS, Config, get_config
 from .generator import (
     bf16_bits_to_f32,
+    count_permutation,
     dirichlet_capacities,
     f64_to_bf16_bits,
     gumbel_retained,
@@ -23,6 +24,7 @@ __all__ = [
     "Config",
     "get_config",
     "bf16_bits_to_f32",
+    "count_permutation",
     "f64_to_bf16_bits",
     "dirichlet_capacities",
     "gumbel_retained",

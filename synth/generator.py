@@ -37,6 +37,7 @@ from .configs import Config
 _CAPACITY_STREAM = 1_000_003
 _GUMBEL_STREAM = 2
 _QUERY_STREAM = 3
+_PERM_STREAM = 4
 
 
 def _head_rng(cfg: Config, g: int, *extra: int) -> np.random.Generator:
@@ -309,3 +310,20 @@ def make_queries(cfg: Config, g: int, Gq: int = 4, W: int = 32, N: int | None = 
     out[..., :half] = a * cos - b * sin
     out[..., half:] = a * sin + b * cos
     return f64_to_bf16_bits(out)
+
+
+def count_permutation(cfg: Config, g: int, capacity: int, seed: int, N: int | None = None) -> np.ndarray:
+    """A seeded permutation of head ``g``'s unprotected positions (int32 [N]):
+    position i takes the count of position perm[i].  Protected positions (the
+    first min(sink, b) and the last min(recent, b - s) for capacity b) map to
+    themselves.  ``seed`` picks one of the fixed permutations (the pages use
+    three fixed seeds: 11, 29 and 47)."""
+    N = cfg.N if N is None else int(N)
+    b = int(min(max(int(capacity), 0), N))
+    s = min(cfg.sink, b)
+    r = min(cfg.recent, b - s)
+    perm = np.arange(N, dtype=np.int64)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), cfg.cfg_id, int(g), _PERM_STREAM])))
+    free = np.arange(s, N - r)
+    perm[free] = rng.permutation(free)
+    return perm.astype(np.int32)

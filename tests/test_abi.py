@@ -18,7 +18,7 @@ def test_library_exports_every_header_symbol():
     declared = krs.header_symbols()
     assert declared == ["twinkv_allocate", "twinkv_allocate_workspace_bytes", "twinkv_gather_kv", "twinkv_repair",
                         "twinkv_score", "twinkv_select", "twinkv_status_string", "twinkv_uniform_capacity",
-                        "twinkv_workspace_bytes"]
+                        "twinkv_uniform_capacity_ceil", "twinkv_variant_score", "twinkv_workspace_bytes"]
     for name in declared:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
@@ -151,3 +151,29 @@ def test_allocate_validation():
                                None) == L.ERR_ARG  # no capacity output
     assert lib.twinkv_allocate(ctypes.byref(p), 8, 4, 32, 7, 500, FAKE, FAKE, FAKE, None, None, FAKE, nb - 1, None,
                                None) == L.ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("N,r", [(10, 0.55), (172, 0.75), (32768, 0.5), (131072, 0.75), (7, 0.0), (7, 1.0), (0, 0.3)])
+def test_ceil_capacity_matches_oracle(N, r):
+    assert krs.uniform_capacity_ceil(N, r) == O.ceil_budget(N, r)
+
+
+def test_variant_validation():
+    lib = krs.load()
+    p = L.params(2, 8, 0, 0.0, 0)
+    other = ctypes.c_void_p(0x200000)
+    third = ctypes.c_void_p(0x300000)
+    cases = [
+        (5, FAKE, FAKE, other, third),       # unknown variant
+        (-1, FAKE, FAKE, other, third),
+        (0, None, FAKE, other, third),       # no counts
+        (0, FAKE, None, other, third),       # no energies
+        (0, FAKE, FAKE, None, third),        # no score output
+        (0, FAKE, FAKE, other, other),       # score and tie alias
+        (0, FAKE, other, other, third),      # score overwrites the energies
+    ]
+    for variant, cnt, en, sc, tie in cases:
+        assert lib.twinkv_variant_score(ctypes.byref(p), variant, cnt, en, None, sc, tie, None, None) == L.ERR_ARG
+    assert lib.twinkv_variant_score(ctypes.byref(L.params(0, 8, 0, 0.0, 0)), 0, FAKE, other, None, third,
+                                    ctypes.c_void_p(0x400000), None, None) == L.ERR_ARG
+    assert krs.uniform_capacity_ceil(-1, 0.5) == -1 and krs.uniform_capacity_ceil(5, 1.5) == -1

@@ -583,3 +583,64 @@ def test_prefix_attention_closed_forms():
     assert abs(z1.sum() - W) < 1e-12
     z7 = O.prefix_attention_scores(K, Q, pool=7)
     np.testing.assert_allclose(z7, [expect[max(0, i - 3):i + 4].max() for i in range(N)], rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# score variants: the standalone count score of the TwinKV page (Eq. 3) and
+# the ablations of the frequency-correction page (sections 5.3 and 5.5)
+
+
+def test_variant_value_only_is_energy_topk():
+    rng = np.random.default_rng(21)
+    for trial in range(20):
+        N = int(rng.integers(8, 14))
+        cap = int(rng.integers(0, N + 1))
+        e = np.round(rng.random(N) * 4, 1)  # coarse: ties happen
+        c = rng.integers(0, 4, N)
+        sc, tie = O.variant_scores(e, c, N, "value")
+        _, idx = O.select_head(sc, tie, cap, 1, 2)
+        assert idx.tolist() == brute.select_exhaustive(e, e, cap, 1, 2)
+
+
+def test_variant_rarity_ranks_counts_then_position():
+    """Removing value: lowest counts first, equal counts to the lower position;
+    the same order as the TwinKV page's s = -r/n."""
+    N = 12
+    c = np.array([0, 5, 1, 1, 0, 3, 2, 0, 1, 4, 0, 0])
+    e = np.arange(N, dtype=float)[::-1] + 1  # energies must not matter
+    sc, tie = O.variant_scores(e, c, N, "rarity")
+    keep, idx = O.select_head(sc, tie, 7, 1, 2)  # protected {0, 10, 11}; 4 more by (count, position)
+    assert idx.tolist() == [0, 2, 3, 4, 7, 10, 11]
+    neg = -c / N  # Eq. 3 directly, with the lower position on ties
+    cand = np.arange(1, 10)
+    order = cand[np.lexsort((cand, -neg[cand]))]
+    assert sorted(order[:4].tolist()) == [2, 3, 4, 7]
+
+
+def test_variant_twin_matches_score_and_permutation_keeps_multiset():
+    from synth import count_permutation, get_config
+    cfg = get_config(2).with_(N=300)
+    rng = np.random.default_rng(3)
+    N = 300
+    e = rng.random(N) * 10
+    c = rng.integers(0, 9, N)
+    sc, tie = O.variant_scores(e, c, N, "twin")
+    assert np.array_equal(sc, O.frequency_score(e, c, N)[0]) and np.array_equal(tie, e)
+    sc_id, _ = O.variant_scores(e, c, N, "twin", perm=np.arange(N))
+    assert np.array_equal(sc_id, sc)
+    cap = 150
+    perms = [count_permutation(cfg, 5, cap, seed) for seed in (11, 29, 47)]
+    s_cnt, r_cnt = O.protected_counts(cap, cfg.sink, cfg.recent)
+    for p in perms:
+        assert np.array_equal(np.sort(p), np.arange(N))
+        assert np.array_equal(p[:s_cnt], np.arange(s_cnt)) and np.array_equal(p[N - r_cnt:], np.arange(N - r_cnt, N))
+        cp = c[p]
+        assert np.array_equal(np.sort(cp[s_cnt:N - r_cnt]), np.sort(c[s_cnt:N - r_cnt]))
+    assert not np.array_equal(perms[0], perms[1])
+
+
+def test_ceil_budget_differs_from_floor():
+    """The TwinKV page keeps ceil((1-rho) n), the frequency page floor(N(1-r))."""
+    assert O.ceil_budget(10, 0.55) == 5 and O.uniform_budget(10, 0.55) == 4
+    assert O.ceil_budget(32768, 0.5) == O.uniform_budget(32768, 0.5) == 16384
+    assert O.ceil_budget(7, 0.0) == 7 and O.ceil_budget(7, 1.0) == 0
