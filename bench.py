@@ -15,7 +15,8 @@ removal.
 Prints one JSON line.  `value` is keys (head positions) through the whole path
 per second.  `gather_kv` times, outside the step, the packed cache of the
 last step's selection (retained keys and values in sequence order),
-`variant_score` the keys of the permuted-count variant, and `allocate` the per-head capacities from the attention of the last 32
+`variant_score` the keys of the permuted-count variant, `count_stats` the
+per-head count statistics against value-only selection, and `allocate` the per-head capacities from the attention of the last 32
 synthetic prefix queries of each KV head (8 KV heads per layer).  `roofline` is for the dominant kernel, the score-mode Gram
 sweep, timed with HIP events that the library records around its launch on
 the stream it runs on; its `achieved` counts the algorithmic work, one
@@ -249,6 +250,20 @@ def main():
     variant_bytes = G * N * (4 + 8 + 4 + 4 + 16)  # perm, energy, own and permuted count, score and tie
     del permd, vout, vres
 
+    # count statistics of the last step (Twin selection vs value-only selection)
+    vsel = krs.select(s_out["energy"], s_out["energy"], caps, cfg.sink, cfg.recent, offsets=offsets)
+    sev = [krs.Events(2) for _ in range(args.steps)]
+    for k in range(args.steps + 1):
+        sres = krs.count_stats(s_out["count"], s_out["energy"], caps, cfg.sink, cfg.recent,
+                               keep_twin=sel_out["keep"], keep_value=vsel["keep"], events=sev[k - 1] if k else None)
+    torch.cuda.synchronize()
+    stats_ms = float(np.mean([e.elapsed_ms(0, 1) for e in sev]))
+    for e in sev:
+        e.close()
+    st_np = sres["stats"].cpu().numpy()
+    stats_bytes = G * N * (4 + 8 + 1 + 1) * 2  # count, energy and both masks, read twice
+    del vsel
+
     # per-head capacities from prefix attention, 8 KV heads per layer
     # (not part of the timed step)
     from synth import make_queries
@@ -320,6 +335,9 @@ def main():
         "variant_score": {"ms": variant_ms, "variant": "twin with permuted counts (seed 11)",
                           "GBs": variant_bytes / (variant_ms * 1e-3) / 1e9,
                           "frac_hbm": variant_bytes / (variant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "count_stats": {"ms": stats_ms, "GBs": stats_bytes / (stats_ms * 1e-3) / 1e9,
+                        "twin_fraction": float(st_np[:, 1].sum() / st_np[:, 0].sum()),
+                        "selection_change_vs_value_only": float(st_np[:, 9].sum() / max(1, st_np[:, 8].sum()))},
         "allocate": {"ms": sum(alloc_ms), "stats_ms": alloc_ms[0], "aggregate_pool_ms": alloc_ms[1],
                      "rank_eq5_ms": alloc_ms[2], "heads_per_layer": Hkv, "queries_per_head": nq,
                      "logit_fp64_tflops": logit_flops / (alloc_ms[0] * 1e-3) / 1e12,

@@ -17,18 +17,22 @@
  *   twinkv_gather_kv  the packed, unpadded cache of the retained keys and
  *                  values in sequence order;
  *   twinkv_allocate  per-head capacities of a layer from the attention of
- *                  its last observed prefix queries.
+ *                  its last observed prefix queries;
+ *   twinkv_count_stats  per-head count statistics (twin fraction, count
+ *                  histogram, discount mean, selection change, margins).
  *
  * Sources (page title and section/equation):
  *   [P1] "TwinKV: A Composable Repair Pass for KV Cache Eviction via Pairwise
  *        Key Redundancy" (arXiv HTML): section 3.1, section 3.2 (Eq. 1, Eq. 2,
- *        Eq. 3, protected regions), section 3.4 (Eq. 4, orphans, donors, swap).
+ *        Eq. 3, protected regions), section 3.4 (Eq. 4, orphans, donors, swap),
+ *        Figure 1(b) (fraction of keys with a twin).
  *   [P2] "Small Frequency Corrections Can Change What Survives KV Cache
  *        Compression" (paperpeel): section 3.1 (budget, protection), section
  *        3.2 (count, energy, score, ties), section 3.3 (head allocation,
  *        Equation 5), section 3.4 (selection order and physical cache
- *        layout), sections 5.3 and 5.5 (score ablations), appendices A.2,
- *        A.3 (prefix attention, budget proof).
+ *        layout), sections 2.1, 5.3 and 5.5 (count statistics, score
+ *        ablations), appendices A.2, A.3 (prefix attention, budget proof),
+ *        B.2 (measured frequency statistics).
  *
  * Conventions for every entry point:
  *   - Array arguments are DEVICE pointers owned by the caller; the library
@@ -90,7 +94,10 @@ enum { TWINKV_OP_SCORE = 0, TWINKV_OP_SELECT = 1, TWINKV_OP_REPAIR = 2 };
 
 /* Phase counts for the `marks` argument. */
 enum { TWINKV_SCORE_PHASES = 2, TWINKV_SELECT_PHASES = 1, TWINKV_REPAIR_PHASES = 4, TWINKV_GATHER_PHASES = 1,
-       TWINKV_ALLOC_PHASES = 3, TWINKV_VARIANT_PHASES = 1 };
+       TWINKV_ALLOC_PHASES = 3, TWINKV_VARIANT_PHASES = 1, TWINKV_STATS_PHASES = 1 };
+
+/* Number of int64 counts per head written by twinkv_count_stats. */
+enum { TWINKV_STAT_INTS = 26 };
 
 /* Score variants for twinkv_variant_score. */
 enum { TWINKV_VARIANT_TWIN = 0, TWINKV_VARIANT_VALUE = 1, TWINKV_VARIANT_RARITY = 2 };
@@ -200,6 +207,35 @@ int twinkv_repair(const twinkv_params* params, const void* keys, const uint8_t* 
  */
 int twinkv_variant_score(const twinkv_params* params, int variant, const int32_t* count, const double* energy,
                          const int32_t* perm, double* score, double* tie, hipStream_t stream, hipEvent_t* marks);
+
+/*
+ * twinkv_count_stats - statistics of every head over its unprotected
+ * positions (the protection of twinkv_select, clipped against capacity[g])
+ * ([P1] Figure 1(b); [P2] sections 2.1 and 5.5, appendix B.2).  Per head g,
+ * stats[g][k] (int64):
+ *   0  n        unprotected positions
+ *   1  twin     of them with count >= 1
+ *   2-7         six-bin count histogram: {0}, {1}, {2}, {3,4}, {5..8}, {9+}
+ *   8  kept     unprotected positions kept by keep_twin
+ *   9  added    kept by keep_twin, not by keep_value
+ *   10 removed  kept by keep_value, not by keep_twin
+ *   11-15       |e/e_cut - 1| of the added positions in five bins with edges
+ *               0.05, 0.10, 0.25, 0.50 (bin k: edges <= value, counted)
+ *   16-20       the same for the removed positions
+ *   21-25       the same for all unprotected positions
+ * and fstats[g][0] = sum of ln((N+1)/(c+1))/ln(N+1) over the unprotected
+ * positions, fstats[g][1] = e_cut, the lowest energy among the unprotected
+ * positions keep_value keeps (0 if none; margins are then all 0).
+ * [P2] measures selection change as added / kept and the discount mean as
+ * fstats[0] / n.  The page's bin edges are not printed; these are readings.
+ *   count: int32 [G][N] (>= 0); energy: double [G][N]; capacity: int32 [G]
+ *   keep_twin, keep_value: uint8 [G][N] (both NULL: entries 8-25 are 0)
+ *   stats: int64 [G][TWINKV_STAT_INTS]; fstats: double [G][2]
+ * Of the parameters G, N, sink and recent are read.  Phases: 0 = statistics.
+ */
+int twinkv_count_stats(const twinkv_params* params, const int32_t* count, const double* energy,
+                       const uint8_t* keep_twin, const uint8_t* keep_value, const int32_t* capacity, int64_t* stats,
+                       double* fstats, hipStream_t stream, hipEvent_t* marks);
 
 /*
  * twinkv_gather_kv - physical cache layout of a selection ([P2] section 3.4):

@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     Params,
     TwinKVError,
     capacity_offsets,
+    count_stats,
     gather_kv,
     header_symbols,
     load,

@@ -23,6 +23,8 @@ OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 OP_SCORE, OP_SELECT, OP_REPAIR = 0, 1, 2
 SCORE_PHASES, SELECT_PHASES, REPAIR_PHASES, GATHER_PHASES, ALLOC_PHASES, VARIANT_PHASES = 2, 1, 4, 1, 3, 1
 VARIANTS = {"twin": 0, "value": 1, "rarity": 2}
+STAT_INTS = 26
+STATS_PHASES = 1
 
 
 class Params(ctypes.Structure):
@@ -80,6 +82,8 @@ def load():
     lib.twinkv_uniform_capacity_ceil.restype = i64
     lib.twinkv_variant_score.argtypes = [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
     lib.twinkv_variant_score.restype = ctypes.c_int
+    lib.twinkv_count_stats.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.twinkv_count_stats.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -413,3 +417,34 @@ def variant_score(count_t, energy_t, variant, perm=None, out=None, events=None):
                                   _ptr(sc), _ptr(tie), _stream(), _marks(events, VARIANT_PHASES))
     _check(st, "twinkv_variant_score")
     return {"score": sc, "tie": tie}
+
+
+def count_stats(count_t, energy_t, capacity, sink=4, recent=64, keep_twin=None, keep_value=None, events=None):
+    """Per-head count statistics over the unprotected positions: int64
+    [G][26] counts (n, twin, six-bin histogram, kept, added, removed and three
+    five-bin margin histograms) and float64 [G][2] (discount sum, value-only
+    energy cut), as device tensors."""
+    lib = load()
+    G, N = count_t.shape
+    dev = count_t.device
+    if count_t.dtype != torch.int32 or not count_t.is_contiguous() or not count_t.is_cuda:
+        raise ValueError("count must be a contiguous int32 device tensor [G][N]")
+    if energy_t.dtype != torch.float64 or tuple(energy_t.shape) != (G, N) or energy_t.device != dev:
+        raise ValueError("energy must be float64 [G][N] on the counts' device")
+    if (keep_twin is None) != (keep_value is None):
+        raise ValueError("give both selections or neither")
+    for t, nm in ((keep_twin, "keep_twin"), (keep_value, "keep_value")):
+        if t is not None and (t.dtype != torch.uint8 or tuple(t.shape) != (G, N) or t.device != dev
+                              or not t.is_contiguous()):
+            raise ValueError(f"{nm} must be contiguous uint8 [G][N] on the counts' device")
+    cap = capacity if torch.is_tensor(capacity) and capacity.device == dev else \
+        torch.as_tensor(capacity, dtype=torch.int32).to(dev)
+    if cap.dtype != torch.int32 or cap.numel() != G:
+        raise ValueError("capacity must be int32 [G]")
+    st = torch.empty((G, STAT_INTS), dtype=torch.int64, device=dev)
+    fs = torch.empty((G, 2), dtype=torch.float64, device=dev)
+    p = params(G, N, 0, 0.0, 0, sink, recent)
+    rc = lib.twinkv_count_stats(ctypes.byref(p), _ptr(count_t), _ptr(energy_t), _ptr(keep_twin), _ptr(keep_value),
+                                _ptr(cap), _ptr(st), _ptr(fs), _stream(), _marks(events, STATS_PHASES))
+    _check(rc, "twinkv_count_stats")
+    return {"stats": st, "fstats": fs}

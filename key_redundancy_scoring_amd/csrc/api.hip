@@ -149,6 +149,30 @@ int twinkv_variant_score(const twinkv_params* p, int variant, const int32_t* cou
   return TWINKV_OK;
 }
 
+int twinkv_count_stats(const twinkv_params* p, const int32_t* count, const double* energy, const uint8_t* keep_twin,
+                       const uint8_t* keep_value, const int32_t* capacity, int64_t* stats, double* fstats,
+                       hipStream_t stream, hipEvent_t* marks) {
+  TRY(check_sizes(p));
+  if (!count || !energy || !capacity || !stats || !fstats) return TWINKV_ERR_ARG;
+  if ((keep_twin == nullptr) != (keep_value == nullptr)) return TWINKV_ERR_ARG;
+  StatsArgs sa{};
+  sa.count = count;
+  sa.energy = energy;
+  sa.keep_twin = keep_twin;
+  sa.keep_value = keep_value;
+  sa.capacity = capacity;
+  sa.stats = stats;
+  sa.fstats = fstats;
+  sa.G = p->G;
+  sa.N = p->N;
+  sa.sink = p->sink;
+  sa.recent = p->recent;
+  TRY(record(marks, 0, stream));
+  TRY_HIP(launch_stats(sa, stream));
+  TRY(record(marks, 1, stream));
+  return TWINKV_OK;
+}
+
 size_t twinkv_workspace_bytes(int op, const twinkv_params* p) {
   switch (op) {
     case TWINKV_OP_SCORE: return check_params(p) == TWINKV_OK ? score_ws(p) : 0;

@@ -97,6 +97,22 @@ hipError_t launch_attn(const AttnArgs& a, int d, int phase, hipStream_t stream);
 hipError_t launch_alloc(const AllocArgs& a, hipStream_t stream);
 hipError_t launch_fill_capacity(int32_t* capacity, int32_t* g_count, int64_t G, int32_t B, hipStream_t stream);
 
+// Count statistics (stats.hip): int64 [G][kStatInts] counts and double
+// [G][2] (sum of normalised discounts, value-only energy cut) per head.
+constexpr int kStatInts = 26;
+struct StatsArgs {
+  const int32_t* count;
+  const double* energy;
+  const uint8_t* keep_twin;   // may be null (then keep_value is null too)
+  const uint8_t* keep_value;
+  const int32_t* capacity;
+  int64_t* stats;
+  double* fstats;
+  int64_t G, N;
+  int32_t sink, recent;
+};
+hipError_t launch_stats(const StatsArgs& a, hipStream_t stream);
+
 struct SwapArgs {
   const uint8_t* keep_in;
   const double* best;

@@ -18,7 +18,7 @@ Sources (cited by page title and section / equation; no line numbers):
   energy, discounted score, tie rule), section 3.3 head allocation from prefix
   attention (Equation 5), section 3.4 selection in sequence order and the
   packed, unpadded cache layout, appendix A.2 prefix-attention statistics,
-  appendix A.3 budget conservation,
+  appendix A.3 budget conservation, appendix B.2 measured count statistics,
   appendix A.1 boundary handling and the Figure 3 example.
 
 Every quantity is evaluated straight from its definition in float64.  Keys and
@@ -48,7 +48,11 @@ design notes of the repository as well):
   max-pool window of 7 is centred and cut at the ends of the prefix, and
   pooling comes before protected positions are excluded; the scores are
   evaluated in float64 and rounded once to float32, the precision the page
-  names, and the global ranking compares those float32 values.
+  names, and the global ranking compares those float32 values;
+* count statistics (P2 B.2): the six histogram bins are {0}, {1}, {2}, {3,4},
+  {5..8}, {9+} and the five margin bins have edges 5%, 10%, 25%, 50% (the
+  page prints neither); every position is counted where the page samples
+  at most 16 per group.
 """
 from __future__ import annotations
 
@@ -334,6 +338,64 @@ def repair_head(K: np.ndarray, retained: np.ndarray, tau: float, window: int, si
         "m": int(m),
         "pairs": pairs.astype(np.int64),
     }
+
+
+# ----------------------------------------------------------------------------
+# count statistics: [P1] section 2 / Figure 1(b), [P2] sections 2.1, 5.5 and
+# appendix B.2
+
+COUNT_BINS = ((0, 0), (1, 1), (2, 2), (3, 4), (5, 8), (9, None))  # six-bin histogram
+MARGIN_EDGES = (0.05, 0.10, 0.25, 0.50)                           # five margin bins
+
+
+def count_stats(count: np.ndarray, energy: np.ndarray, keep_twin: np.ndarray, keep_value: np.ndarray,
+                capacity: int, sink: int, recent: int) -> dict:
+    """Statistics of one head over its unprotected positions (protection
+    clipped against ``capacity`` as in the selection):
+
+    * n: unprotected positions; twin: those with at least one nonlocal twin
+      (c >= 1, the fraction of [P1] Figure 1(b) and [P2] section 2.1);
+    * hist: the six-bin count histogram of [P2] Figure 1 / B.2, bins
+      {0}, {1}, {2}, {3,4}, {5..8}, {9+} (the page does not print its edges);
+    * omega_sum: sum of the normalised discounts ln((N+1)/(c+1))/ln(N+1)
+      (the mean of [P2] section 5.5 is omega_sum / n);
+    * kept, added, removed: unprotected positions retained by the Twin
+      selection, retained by Twin but not by value-only, and the reverse
+      (selection change = added / kept, [P2] B.2);
+    * e_cut: the lowest unprotected energy value-only retains (0 if none);
+      margins_added / _removed / _pool: |e/e_cut - 1| of the Twin-added, the
+      Twin-removed and all unprotected positions in five bins with edges
+      5%, 10%, 25%, 50% ([P2] B.2 counts every position, where the page
+      samples at most 16 per group; its edges are not printed)."""
+    c = np.asarray(count, dtype=np.int64)
+    e = np.asarray(energy, dtype=np.float64)
+    N = c.shape[0]
+    prot = protected_mask(N, int(capacity), sink, recent)
+    u = ~prot
+    kt = (np.asarray(keep_twin) != 0) & u
+    kv = (np.asarray(keep_value) != 0) & u
+    cu = c[u]
+    hist = []
+    for lo, hi in COUNT_BINS:
+        m = cu >= lo if hi is None else (cu >= lo) & (cu <= hi)
+        hist.append(int(m.sum()))
+    omega = np.log((N + 1.0) / (cu + 1.0)) / math.log(N + 1.0)
+    e_cut = float(e[kv].min()) if kv.any() else 0.0
+
+    def margins(mask):
+        out = [0] * (len(MARGIN_EDGES) + 1)
+        if e_cut <= 0.0:
+            return out
+        dev = np.abs(e[mask] / e_cut - 1.0)
+        for x in dev:
+            out[int(np.searchsorted(MARGIN_EDGES, x, side="right"))] += 1
+        return out
+
+    added = kt & ~kv
+    removed = kv & ~kt
+    return {"n": int(u.sum()), "twin": int((cu >= 1).sum()), "hist": hist, "omega_sum": float(omega.sum()),
+            "kept": int(kt.sum()), "added": int(added.sum()), "removed": int(removed.sum()), "e_cut": e_cut,
+            "margins_added": margins(added), "margins_removed": margins(removed), "margins_pool": margins(u)}
 
 
 # ----------------------------------------------------------------------------

@@ -16,7 +16,8 @@ FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: every call belo
 def test_library_exports_every_header_symbol():
     lib = krs.load()
     declared = krs.header_symbols()
-    assert declared == ["twinkv_allocate", "twinkv_allocate_workspace_bytes", "twinkv_gather_kv", "twinkv_repair",
+    assert declared == ["twinkv_allocate", "twinkv_allocate_workspace_bytes", "twinkv_count_stats",
+                        "twinkv_gather_kv", "twinkv_repair",
                         "twinkv_score", "twinkv_select", "twinkv_status_string", "twinkv_uniform_capacity",
                         "twinkv_uniform_capacity_ceil", "twinkv_variant_score", "twinkv_workspace_bytes"]
     for name in declared:
@@ -177,3 +178,16 @@ def test_variant_validation():
     assert lib.twinkv_variant_score(ctypes.byref(L.params(0, 8, 0, 0.0, 0)), 0, FAKE, other, None, third,
                                     ctypes.c_void_p(0x400000), None, None) == L.ERR_ARG
     assert krs.uniform_capacity_ceil(-1, 0.5) == -1 and krs.uniform_capacity_ceil(5, 1.5) == -1
+
+
+def test_count_stats_validation():
+    lib = krs.load()
+    p = L.params(2, 8, 0, 0.0, 0)
+    A, B_, C, D, E, F = (ctypes.c_void_p(x) for x in (0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000))
+    ok_args = [A, B_, None, None, C, D, E]
+    for k in (0, 1, 4, 5, 6):  # count, energy, capacity, stats, fstats are required
+        args = list(ok_args)
+        args[k] = None
+        assert lib.twinkv_count_stats(ctypes.byref(p), *args, None, None) == L.ERR_ARG
+    assert lib.twinkv_count_stats(ctypes.byref(p), A, B_, F, None, C, D, E, None, None) == L.ERR_ARG  # one selection
+    assert lib.twinkv_count_stats(ctypes.byref(L.params(2, 0, 0, 0.0, 0)), *ok_args, None, None) == L.ERR_ARG

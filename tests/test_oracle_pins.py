@@ -644,3 +644,53 @@ def test_ceil_budget_differs_from_floor():
     assert O.ceil_budget(10, 0.55) == 5 and O.uniform_budget(10, 0.55) == 4
     assert O.ceil_budget(32768, 0.5) == O.uniform_budget(32768, 0.5) == 16384
     assert O.ceil_budget(7, 0.0) == 7 and O.ceil_budget(7, 1.0) == 0
+
+
+# ---------------------------------------------------------------------------
+# count statistics (Figure 1(b) of the TwinKV page; section 2.1, 5.5 and B.2
+# of the frequency-correction page)
+
+
+def test_count_stats_hand_example():
+    """Capacity 8 with one sink and two recent slots protects {0, 12, 13};
+    the 11 unprotected positions 1..11 have counts 0,1,2,3,4,5,8,9,30,0,1."""
+    N = 14
+    c = np.array([7, 0, 1, 2, 3, 4, 5, 8, 9, 30, 0, 1, 6, 0])
+    e = np.array([1, 10, 9, 8, 7, 6, 5, 4, 3, 2, 1.2, 1.1, 1, 1], dtype=float)
+    kv = np.zeros(N, np.uint8)
+    kv[[0, 1, 2, 3, 4, 12, 13]] = 1  # value-only keeps energies 10, 9, 8, 7: the cut is 7
+    kt = kv.copy()
+    kt[4] = 0
+    kt[10] = 1  # Twin drops position 4 (e 7) for position 10 (e 1.2)
+    st = O.count_stats(c, e, kt, kv, 8, 1, 2)
+    assert st["n"] == 11 and st["twin"] == 9
+    assert st["hist"] == [2, 2, 1, 2, 2, 2]
+    cu = np.array([0, 1, 2, 3, 4, 5, 8, 9, 30, 0, 1])
+    assert abs(st["omega_sum"] - sum(math.log(15 / (x + 1)) / math.log(15) for x in cu)) < 1e-12
+    assert (st["kept"], st["added"], st["removed"], st["e_cut"]) == (4, 1, 1, 7.0)
+    assert st["margins_added"] == [0, 0, 0, 0, 1]     # |1.2/7 - 1| = 0.83
+    assert st["margins_removed"] == [1, 0, 0, 0, 0]   # the cut itself
+    assert st["margins_pool"] == [1, 0, 2, 4, 4]
+
+
+def test_count_stats_planted_fraction():
+    """On a synthetic head the twin fraction is the share of planted cluster
+    members with a mate outside the window (the planted structure predicts
+    every count, see the cluster pin above)."""
+    from synth import get_config, make_head
+    cfg = get_config(2)
+    N = 2000
+    h = make_head(cfg, 1, N=N)
+    r = O.score_head(h["K"], h["V"], cfg.tau, cfg.window)
+    cap = O.uniform_budget(N, 0.5)
+    kt, _ = O.select_head(r["score"], r["energy"], cap, cfg.sink, cfg.recent)
+    kv, _ = O.select_head(r["energy"], r["energy"], cap, cfg.sink, cfg.recent)
+    st = O.count_stats(r["count"], r["energy"], kt, kv, cap, cfg.sink, cfg.recent)
+    prot = O.protected_mask(N, cap, cfg.sink, cfg.recent)
+    cl = h["cluster"]
+    pos = np.arange(N)
+    has_mate = np.array([cl[i] >= 0 and np.any((cl == cl[i]) & (np.abs(pos - i) > cfg.window)) for i in range(N)])
+    assert st["twin"] == int((has_mate & ~prot).sum())
+    assert sum(st["hist"]) == st["n"] == int((~prot).sum())
+    assert st["kept"] == cap - int(prot.sum())
+    assert st["added"] == st["removed"]  # both selections keep the same number
