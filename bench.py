@@ -53,13 +53,13 @@ GRAM_SOURCE = os.path.join(ROOT, "key_redundancy_scoring_amd", "csrc", "gram.hip
 # reading for a plain device copy of known size; keyed by the sha256 of the
 # Gram source the counters were taken on.
 MEASURED_TRAFFIC: dict = {
-    "755c4e4d0f073bb4390c32e5e3b3b74e013565d4c8a9ba706381188423d08a4f": {
+    "60c6a6851daf310bdd7942c45d30e6b4bea3578e13a22e1b837e934bafce878c": {
         "workload": (128, 32768, 64),
-        # FETCH_SIZE 2013097.75 KiB x 1.99994 (a 1 GiB copy reads 524304 KiB),
-        # WRITE_SIZE 196608 KiB x 1.0 (the same copy writes 1048576 KiB)
-        "fetch_bytes": 4122700933,
-        "write_bytes": 201326592,
-        "bytes_per_launch": 4324027525,
+        # FETCH_SIZE 2125983.3 KiB x 1.99994 (a 1 GiB copy reads 524304 KiB),
+        # WRITE_SIZE 253978.2 KiB x 1.0 (the same copy writes 1048576 KiB)
+        "fetch_bytes": 4353883178,
+        "write_bytes": 260073677,
+        "bytes_per_launch": 4613956855,
     },
 }
 
