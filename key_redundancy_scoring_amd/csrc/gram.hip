@@ -327,18 +327,20 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
   // Epilogue of block b of a tile whose dots are in acc: y = dot * rinv_j, the
   // block maximum (neutralised to -inf on a masked tile by neg), running
   // maximum and first tile, count when some lane crosses tau*||k_i||.
-  auto epilogue = [&](f32x16& acc, int b, const float (&rv)[16], float neg, int tile) TWINKV_INLINE {
+  auto epilogue = [&](f32x16& acc, int b, const float (&rv)[16], bool live, int tile) TWINKV_INLINE {
     float yy[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       acc[r] *= rv[r];
       yy[r] = acc[r];
     }
-    const float m = __builtin_fminf(max16(yy), neg);
-    btile[b] = m > best[b] ? tile : btile[b];
-    best[b] = __builtin_fmaxf(best[b], m);
-    if (MODE == GRAM_SCORE) {
-      if (__ballot(m > thr[b]) != 0ull) count16(acc, b);
+    const float m = max16(yy);
+    if (live) {  // wave-uniform: a masked tile leaves the state alone
+      btile[b] = m > best[b] ? tile : btile[b];
+      best[b] = __builtin_fmaxf(best[b], m);
+      if (MODE == GRAM_SCORE) {
+        if (__ballot(m > thr[b]) != 0ull) count16(acc, b);
+      }
     }
   };
   // Keep the next tile's MFMAs between the epilogue's vector instructions.
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
   const int nstages = (ncols + SC - 1) / SC;
   f32x16 acc[RB];
   bf16x8 A[KS];
-  float rv[16], rv_next[16];
+  float rv[16];
   int band_lo = INT_MAX, band_hi = -1;  // masked tiles other than the tail
   if (nstages > 0) issue(0, buf0);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -385,36 +387,32 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
     for (int tt = 0; tt < TILES - 1; ++tt) {
       const int tile = st * TILES + tt;
       load_a(cur, tt + 1, (tt + 1) & 1, A);
-      load_rv(cur, tt + 1, rv_next);
-      const float neg = ((mbits >> tt) & 1u) ? -__builtin_inff() : __builtin_inff();
+      const bool live = ((mbits >> tt) & 1u) == 0u;
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
-        epilogue(acc[b], b, rv, neg, tile);
+        epilogue(acc[b], b, rv, live, tile);
         mfma_block(A, b, acc[b]);
         interleave();
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) rv[r] = rv_next[r];
+      // this tile's inverse norms are no longer needed: fetch the next tile's
+      // into the same registers while the last block's MFMAs run
+      load_rv(cur, tt + 1, rv);
     }
     // every operand of this stage has been read: publish the next one
     const bool more = st + 1 < nstages;
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     if (st + 2 < nstages) issue((st + 2) * SC, cur);
-    if (more) {
-      load_a(nxt, 0, 0, A);
-      load_rv(nxt, 0, rv_next);
-    }
+    if (more) load_a(nxt, 0, 0, A);
     const int tile = st * TILES + TILES - 1;
-    const float neg = ((mbits >> (TILES - 1)) & 1u) ? -__builtin_inff() : __builtin_inff();
+    const bool live = ((mbits >> (TILES - 1)) & 1u) == 0u;
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
-      epilogue(acc[b], b, rv, neg, tile);
+      epilogue(acc[b], b, rv, live, tile);
       if (more) mfma_block(A, b, acc[b]);
       interleave();
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) rv[r] = rv_next[r];
+    if (more) load_rv(nxt, 0, rv);
   };
 #pragma unroll 1
   for (int st = 0; st < nstages; st += 2) {
