@@ -53,13 +53,13 @@ GRAM_SOURCE = os.path.join(ROOT, "key_redundancy_scoring_amd", "csrc", "gram.hip
 # reading for a plain device copy of known size; keyed by the sha256 of the
 # Gram source the counters were taken on.
 MEASURED_TRAFFIC: dict = {
-    "60c6a6851daf310bdd7942c45d30e6b4bea3578e13a22e1b837e934bafce878c": {
+    "c5cba660789593d57081e8646751e56fa6a00d83776bbcd985add954f3c66c8f": {
         "workload": (128, 32768, 64),
-        # FETCH_SIZE 2125983.3 KiB x 1.99994 (a 1 GiB copy reads 524304 KiB),
-        # WRITE_SIZE 253978.2 KiB x 1.0 (the same copy writes 1048576 KiB)
-        "fetch_bytes": 4353883178,
-        "write_bytes": 260073677,
-        "bytes_per_launch": 4613956855,
+        # FETCH_SIZE 2221417.9 KiB x 1.99995 (a 1 GiB copy reads 524301.4 KiB),
+        # WRITE_SIZE 98304.0 KiB x 1.0 (the same copy writes 1048576 KiB)
+        "fetch_bytes": 4549347585,
+        "write_bytes": 100663296,
+        "bytes_per_launch": 4650010881,
     },
 }
 

@@ -50,10 +50,17 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
+// d = 64: the queries sit in LDS widened to fp64 (64 KiB) and the key in
+// fp64 registers, so each product is one fp64 FMA of exact operands.  d = 128
+// (whose fp64 key would not fit the registers) keeps bf16 queries in LDS and
+// forms each exact product in fp32 before the fp64 sum.  Both sum the d
+// products in order with one rounding each, so they give the same logits.
 template <int D, int PHASE>
 __global__ __launch_bounds__(kAT) void attn_kernel(AttnArgs a) {
   constexpr int CH = D / 8;
-  __shared__ uint4 qs[kMaxQueries * CH];
+  constexpr bool F64 = D == 64;
+  __shared__ uint4 qs[F64 ? 1 : kMaxQueries * CH];
+  __shared__ double qd[F64 ? kMaxQueries * D : 2];
   __shared__ double pm[kAT / 64][kMaxQueries];
   __shared__ double pz[kAT / 64][kMaxQueries];
   __shared__ double sm[kMaxQueries];
@@ -64,7 +71,12 @@ __global__ __launch_bounds__(kAT) void attn_kernel(AttnArgs a) {
   const int Q = a.Gq * a.W;
   const int tid = threadIdx.x;
   const uint4* qg = reinterpret_cast<const uint4*>(a.queries) + (size_t)g * Q * CH;
-  for (int e = tid; e < Q * CH; e += kAT) qs[e] = qg[e];
+  if (F64) {
+    const uint16_t* qh = a.queries + (size_t)g * Q * D;
+    for (int e = tid; e < Q * D; e += kAT) qd[e] = (double)__uint_as_float((uint32_t)qh[e] << 16);
+  } else {
+    for (int e = tid; e < Q * CH; e += kAT) qs[e] = qg[e];
+  }
   if (PHASE == 2) {
     for (int q = tid; q < Q; q += kAT) {
       sm[q] = a.mz[((size_t)g * Q + q) * 2];
@@ -76,7 +88,8 @@ __global__ __launch_bounds__(kAT) void attn_kernel(AttnArgs a) {
   const int64_t N = a.N;
   const int64_t j = chunk * kAT + tid;
   const bool valid = j < N;
-  float kf[D];
+  float kf[F64 ? 1 : D];
+  double kd[F64 ? D : 1];
   {
     const uint4* kj = reinterpret_cast<const uint4*>(a.keys) + ((size_t)g * N + (valid ? j : 0)) * CH;
 #pragma unroll
@@ -85,8 +98,14 @@ __global__ __launch_bounds__(kAT) void attn_kernel(AttnArgs a) {
       const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        kf[8 * c + 2 * t] = __uint_as_float(w[t] << 16);
-        kf[8 * c + 2 * t + 1] = __uint_as_float(w[t] & 0xffff0000u);
+        const float lo = __uint_as_float(w[t] << 16), hi = __uint_as_float(w[t] & 0xffff0000u);
+        if (F64) {
+          kd[8 * c + 2 * t] = (double)lo;
+          kd[8 * c + 2 * t + 1] = (double)hi;
+        } else {
+          kf[8 * c + 2 * t] = lo;
+          kf[8 * c + 2 * t + 1] = hi;
+        }
       }
     }
   }
@@ -95,14 +114,24 @@ __global__ __launch_bounds__(kAT) void attn_kernel(AttnArgs a) {
 #pragma unroll 1
   for (int q = 0; q < Q; ++q) {
     double s = 0.0;
+    if (F64) {
+      const double2* q2 = reinterpret_cast<const double2*>(qd + q * D);
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const uint4 u = qs[q * CH + c];
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      for (int c = 0; c < D / 2; ++c) {
+        const double2 qq = q2[c];  // the same address in every lane: a broadcast
+        s = fma(qq.x, kd[2 * c], s);
+        s = fma(qq.y, kd[2 * c + 1], s);
+      }
+    } else {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        s += (double)(__uint_as_float(w[t] << 16) * kf[8 * c + 2 * t]);        // exact in fp32
-        s += (double)(__uint_as_float(w[t] & 0xffff0000u) * kf[8 * c + 2 * t + 1]);
+      for (int c = 0; c < CH; ++c) {
+        const uint4 u = qs[q * CH + c];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          s += (double)(__uint_as_float(w[t] << 16) * kf[8 * c + 2 * t]);  // exact in fp32
+          s += (double)(__uint_as_float(w[t] & 0xffff0000u) * kf[8 * c + 2 * t + 1]);
+        }
       }
     }
     s *= scale;
