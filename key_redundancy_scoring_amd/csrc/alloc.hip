@@ -17,8 +17,8 @@
 //
 // Kernels:
 //   attn_kernel<D, 1>  one block of 256 keys of one head: every key against
-//                      every observing query, logits in fp64 (bf16 products
-//                      are exact in fp32, summed in fp64); per query the
+//                      every observing query, logits on the fp64 matrix
+//                      cores (exact bf16 products, fp64 sums); per query the
 //                      block's max logit and sum of exp(s - max);
 //   combine_kernel     per query, the block partials merged into (m, Z);
 //   attn_kernel<D, 2>  per key, sum over queries of exp(s - m)/Z, over Gq;
@@ -28,8 +28,8 @@
 //   descending, then pool index ascending = head, then position);
 //   alloc_kernel       per layer: g_h from the selected pool, Equation 5.
 // The logits are recomputed in the second pass rather than stored: storing
-// them would take Gq*W*N*8 bytes per head, while recomputing is FMA work the
-// CUs have to spare.
+// them would take Gq*W*N*8 bytes per head, while recomputing is matrix-core
+// work that runs beside the exponentials on the vector units.
 
 #include "blockops.h"
 #include "internal.h"
@@ -37,118 +37,159 @@
 namespace twinkv {
 namespace {
 
-constexpr int kAT = 256;  // threads (keys) per attention block
+constexpr int kAT = 256;            // threads per attention block = keys per block
+constexpr int kKG = 4;              // key groups of 16 per wave: 64 keys per wave
+constexpr int kQG = kMaxQueries / 16;
 
-__device__ __forceinline__ double wave_max(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
-  return v;
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+// fp64 DPP moves within rows of 16 lanes (both 32-bit halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
 }
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+// Max and sum over the 16 lanes of a row (lane xor 1, xor 2, half-row mirror,
+// row mirror); every lane of the row ends with the same value.
+__device__ __forceinline__ double row16_max(double v) {
+  v = fmax(v, dpp_f64<0xB1>(v));
+  v = fmax(v, dpp_f64<0x4E>(v));
+  v = fmax(v, dpp_f64<0x141>(v));
+  return fmax(v, dpp_f64<0x140>(v));
+}
+__device__ __forceinline__ double row16_sum(double v) {
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  v += dpp_f64<0x141>(v);
+  return v + dpp_f64<0x140>(v);
 }
 
-// d = 64: the queries sit in LDS widened to fp64 (64 KiB) and the key in
-// fp64 registers, so each product is one fp64 FMA of exact operands.  d = 128
-// (whose fp64 key would not fit the registers) keeps bf16 queries in LDS and
-// forms each exact product in fp32 before the fp64 sum.  Both sum the d
-// products in order with one rounding each, so they give the same logits.
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// The logits of one block: 256 keys of one head against its Q = Gq*W
+// observing queries, on the fp64 matrix cores (v_mfma_f64_16x16x4f64: lane l
+// supplies A[l%16][l/16] and B[l/16][l%16] and holds D[l/16 + 4r][l%16],
+// r = 0..3, as measured on gfx950).  A tile is 16 queries x 16 keys; a wave owns 4 key groups (64
+// keys) and walks the query groups.  The feature index of step s in lane
+// group k is (d/4)k + s, so a lane's operands are contiguous slices of a row.
+// The bf16 products are exact in fp64; only the sums round.  The queries are
+// staged once per block in LDS as fp32 (exact), in operand order, so each
+// wave reads one contiguous 1 KiB per four steps; the keys stay in registers
+// as fp32.  Both are widened to fp64 at the matrix core's input.
 template <int D, int PHASE>
 __global__ __launch_bounds__(kAT) void attn_kernel(AttnArgs a) {
-  constexpr int CH = D / 8;
-  constexpr bool F64 = D == 64;
-  __shared__ uint4 qs[F64 ? 1 : kMaxQueries * CH];
-  __shared__ double qd[F64 ? kMaxQueries * D : 2];
+  constexpr int KS = D / 4;  // k-steps per tile
+  constexpr int C8 = D / 8;  // 16-byte chunks per bf16 row
+  __shared__ float4 qa[kQG * (KS / 4) * 64];
   __shared__ double pm[kAT / 64][kMaxQueries];
   __shared__ double pz[kAT / 64][kMaxQueries];
-  __shared__ double sm[kMaxQueries];
-  __shared__ double sr[kMaxQueries];  // 1 / Z
+  __shared__ double2 smr[kMaxQueries];  // (max, 1 / normaliser)
 
   const int64_t g = blockIdx.x / a.nchunk;
   const int64_t chunk = blockIdx.x % a.nchunk;
   const int Q = a.Gq * a.W;
+  const int nqg = (Q + 15) / 16;
   const int tid = threadIdx.x;
-  const uint4* qg = reinterpret_cast<const uint4*>(a.queries) + (size_t)g * Q * CH;
-  if (F64) {
-    const uint16_t* qh = a.queries + (size_t)g * Q * D;
-    for (int e = tid; e < Q * D; e += kAT) qd[e] = (double)__uint_as_float((uint32_t)qh[e] << 16);
-  } else {
-    for (int e = tid; e < Q * CH; e += kAT) qs[e] = qg[e];
+  const int lane = tid & 63, wv = tid >> 6, kq = lane >> 4;
+
+  {
+    const uint4* qsrc = reinterpret_cast<const uint4*>(a.queries) + (size_t)g * Q * C8;
+    for (int e = tid; e < nqg * 16 * C8; e += kAT) {
+      const int qq = e / C8, c = e % C8;
+      const uint4 u = qq < Q ? qsrc[(size_t)qq * C8 + c] : make_uint4(0u, 0u, 0u, 0u);
+      const int f0 = 8 * c;
+      float4* dst = qa + ((qq >> 4) * (KS / 4) + (f0 % KS) / 4) * 64 + (qq & 15) + 16 * (f0 / KS);
+      dst[0] = make_float4(bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y));
+      dst[64] = make_float4(bf_lo(u.z), bf_hi(u.z), bf_lo(u.w), bf_hi(u.w));
+    }
+    if (PHASE == 2) {
+      for (int q = tid; q < nqg * 16; q += kAT) {
+        double2 v = make_double2(0.0, 0.0);
+        if (q < Q) {
+          v.x = a.mz[((size_t)g * Q + q) * 2];
+          v.y = 1.0 / a.mz[((size_t)g * Q + q) * 2 + 1];
+        }
+        smr[q] = v;
+      }
+    }
   }
-  if (PHASE == 2) {
-    for (int q = tid; q < Q; q += kAT) {
-      sm[q] = a.mz[((size_t)g * Q + q) * 2];
-      sr[q] = 1.0 / a.mz[((size_t)g * Q + q) * 2 + 1];
+
+  const int64_t N = a.N;
+  const int64_t j0 = chunk * kAT + wv * 64 + (lane & 15);
+  float kb[kKG][KS];
+#pragma unroll
+  for (int kg = 0; kg < kKG; ++kg) {
+    const int64_t j = j0 + 16 * kg;
+    const int64_t jl = j < N ? j : N - 1;
+    const uint4* src = reinterpret_cast<const uint4*>(a.keys + ((size_t)g * N + jl) * D + KS * kq);
+#pragma unroll
+    for (int c = 0; c < KS / 8; ++c) {
+      const uint4 u = src[c];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        kb[kg][8 * c + 2 * t] = bf_lo(w[t]);
+        kb[kg][8 * c + 2 * t + 1] = bf_hi(w[t]);
+      }
     }
   }
   __syncthreads();
 
-  const int64_t N = a.N;
-  const int64_t j = chunk * kAT + tid;
-  const bool valid = j < N;
-  float kf[F64 ? 1 : D];
-  double kd[F64 ? D : 1];
-  {
-    const uint4* kj = reinterpret_cast<const uint4*>(a.keys) + ((size_t)g * N + (valid ? j : 0)) * CH;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const uint4 u = kj[c];
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float lo = __uint_as_float(w[t] << 16), hi = __uint_as_float(w[t] & 0xffff0000u);
-        if (F64) {
-          kd[8 * c + 2 * t] = (double)lo;
-          kd[8 * c + 2 * t + 1] = (double)hi;
-        } else {
-          kf[8 * c + 2 * t] = lo;
-          kf[8 * c + 2 * t + 1] = hi;
-        }
-      }
-    }
-  }
   const double scale = a.inv_sqrt_d;
-  double acc = 0.0;
+  double agg[kKG] = {};
 #pragma unroll 1
-  for (int q = 0; q < Q; ++q) {
-    double s = 0.0;
-    if (F64) {
-      const double2* q2 = reinterpret_cast<const double2*>(qd + q * D);
+  for (int qg = 0; qg < nqg; ++qg) {
+    v4d acc[kKG];
 #pragma unroll
-      for (int c = 0; c < D / 2; ++c) {
-        const double2 qq = q2[c];  // the same address in every lane: a broadcast
-        s = fma(qq.x, kd[2 * c], s);
-        s = fma(qq.y, kd[2 * c + 1], s);
-      }
-    } else {
+    for (int kg = 0; kg < kKG; ++kg) acc[kg] = v4d{0.0, 0.0, 0.0, 0.0};
+    const float4* ap = qa + qg * (KS / 4) * 64 + lane;
 #pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const uint4 u = qs[q * CH + c];
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    for (int s4 = 0; s4 < KS / 4; ++s4) {
+      const float4 av = ap[s4 * 64];
+      const float af[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          s += (double)(__uint_as_float(w[t] << 16) * kf[8 * c + 2 * t]);  // exact in fp32
-          s += (double)(__uint_as_float(w[t] & 0xffff0000u) * kf[8 * c + 2 * t + 1]);
-        }
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int kg = 0; kg < kKG; ++kg)
+          acc[kg] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)af[u], (double)kb[kg][4 * s4 + u], acc[kg], 0, 0, 0);
       }
     }
-    s *= scale;
-    const int64_t tq = N - a.W + (q % a.W);
-    const bool ok = valid && j <= tq;
-    if (PHASE == 1) {
-      const double m = wave_max(ok ? s : -__builtin_inf());
-      const double e = (ok && m > -__builtin_inf()) ? exp(s - m) : 0.0;
-      const double z = wave_sum(e);
-      if ((tid & 63) == 0) {
-        pm[tid >> 6][q] = m;
-        pz[tid >> 6][q] = z;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int q = qg * 16 + kq + 4 * r;
+      const int64_t tq = N - a.W + (q % a.W);
+      double v[kKG];
+      bool ok[kKG];
+#pragma unroll
+      for (int kg = 0; kg < kKG; ++kg) {
+        const int64_t j = j0 + 16 * kg;
+        ok[kg] = q < Q && j < N && j <= tq;
+        v[kg] = acc[kg][r] * scale;
       }
-    } else {
-      if (ok) acc += exp(s - sm[q]) * sr[q];
+      if (PHASE == 1) {
+        double m = -__builtin_inf();
+#pragma unroll
+        for (int kg = 0; kg < kKG; ++kg) m = fmax(m, ok[kg] ? v[kg] : -__builtin_inf());
+        m = row16_max(m);
+        double z = 0.0;
+#pragma unroll
+        for (int kg = 0; kg < kKG; ++kg) z += ok[kg] ? exp(v[kg] - m) : 0.0;
+        z = row16_sum(z);
+        if ((lane & 15) == 0 && q < Q) {
+          pm[wv][q] = m;
+          pz[wv][q] = z;
+        }
+      } else {
+        const double2 mr = smr[q];
+#pragma unroll
+        for (int kg = 0; kg < kKG; ++kg) agg[kg] += ok[kg] ? exp(v[kg] - mr.x) * mr.y : 0.0;
+      }
     }
   }
+
   if (PHASE == 1) {
     __syncthreads();
     for (int q = tid; q < Q; q += kAT) {
@@ -165,8 +206,15 @@ __global__ __launch_bounds__(kAT) void attn_kernel(AttnArgs a) {
       dst[0] = m;
       dst[1] = z;
     }
-  } else if (valid) {
-    a.agg[(size_t)g * N + j] = acc * a.inv_gq;
+  } else {
+    // the four lane groups of a column hold disjoint query rows of one key
+#pragma unroll
+    for (int kg = 0; kg < kKG; ++kg) {
+      agg[kg] += __shfl_xor(agg[kg], 16);
+      agg[kg] += __shfl_xor(agg[kg], 32);
+      const int64_t j = j0 + 16 * kg;
+      if (kq == 0 && j < N) a.agg[(size_t)g * N + j] = agg[kg] * a.inv_gq;
+    }
   }
 }
 
