@@ -22,11 +22,11 @@
 //                      block's max logit and sum of exp(s - max);
 //   combine_kernel     per query, the block partials merged into (m, Z);
 //   attn_kernel<D, 2>  per key, sum over queries of exp(s - m)/Z, over Gq;
-//   pool_kernel        the width-`pool` max, fp32 z, and the layer's pool of
-//                      unprotected scores in (head, position) order;
-//   the selection kernel over each layer's pool with capacity H*U (score
-//   descending, then pool index ascending = head, then position);
-//   alloc_kernel       per layer: g_h from the selected pool, Equation 5.
+//   pool_kernel        the width-`pool` max, fp32 z;
+//   rank_*_kernel      per layer, the threshold of the H*U largest
+//                      unprotected z (three radix passes over many blocks),
+//                      per head the counts above and at it, then g_h (ties
+//                      to the lower head, then position) and Equation 5.
 // The logits are recomputed in the second pass rather than stored: storing
 // them would take Gq*W*N*8 bytes per head, while recomputing is matrix-core
 // work that runs beside the exponentials on the vector units.
@@ -235,8 +235,7 @@ __global__ __launch_bounds__(kMaxQueries) void combine_kernel(AttnArgs a) {
   a.mz[((size_t)g * Q + q) * 2 + 1] = z;
 }
 
-// z = fp32(max of agg over the centred window), and the layer's pool of
-// unprotected scores, head after head.
+// z = fp32(max of agg over the centred window).
 __global__ __launch_bounds__(kAT) void pool_kernel(AttnArgs a) {
   const int64_t N = a.N;
   const int64_t nb = (N + kAT - 1) / kAT;
@@ -249,47 +248,163 @@ __global__ __launch_bounds__(kAT) void pool_kernel(AttnArgs a) {
   const double* ag = a.agg + (size_t)g * N;
   double m = ag[lo];
   for (int64_t i = lo + 1; i <= hi; ++i) m = fmax(m, ag[i]);
-  const float z = (float)m;
-  a.z[(size_t)g * N + j] = z;
-  if (j >= a.s_cnt && j < N - a.r_cnt) {
-    const int64_t width = N - a.s_cnt - a.r_cnt;
-    a.pool_score[(size_t)g * width + (j - a.s_cnt)] = (double)z;
+  a.z[(size_t)g * N + j] = (float)m;
+}
+
+// The layer-wide ranking of the unprotected z, by a radix select on their
+// fp32 bit patterns (z >= 0, so the bits order as the values).  Three passes
+// over bits 31..21, 20..10 and 9..0 find T, the (H*U)-th largest unprotected
+// z of each layer, and `need`, how many of the entries equal to T the top
+// H*U takes.  Then each head counts its entries above and equal to T.  Equal
+// scores go to the lower head first (then the lower position, which does not
+// change a count), so g_h = above_h + the part of `need` that the heads
+// before h have not used, capped at equal_h.
+constexpr int kRankBins = 2048;
+constexpr int kRT = 256;
+constexpr int kRPer = 16;
+constexpr int kRChunk = kRT * kRPer;  // entries per ranking block
+
+__device__ __forceinline__ int rank_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
+__device__ __forceinline__ int rank_bits(int pass) { return pass == 2 ? 10 : 11; }
+
+__global__ void rank_init_kernel(AllocArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < a.L * kRankBins) a.hist[i] = 0u;
+  if (i < a.G * 3) a.counts[i] = 0u;
+  if (i < a.L) {
+    a.prefix[i] = 0u;
+    a.need[i] = (int64_t)a.H * a.U;
   }
 }
 
-// One block per layer: g_h from the selected pool, then Equation 5.
-__global__ __launch_bounds__(kBT) void alloc_kernel(AllocArgs a) {
-  __shared__ long long red[kBW];
-  __shared__ int cnt[kMaxHeads];
-  __shared__ int anynz;
-  const int64_t layer = blockIdx.x;
-  const int H = a.H;
-  const int64_t width = a.width;
-  const uint8_t* keep = a.pool_keep + (size_t)layer * H * width;
-  const double* sc = a.pool_score + (size_t)layer * H * width;
-  if (threadIdx.x == 0) anynz = 0;
+// Digit histogram of the entries that match the threshold bits found so far.
+__global__ __launch_bounds__(kRT) void rank_hist_kernel(AllocArgs a, int pass) {
+  __shared__ uint32_t h[kRankBins];
+  const int64_t nb = (a.width + kRChunk - 1) / kRChunk;
+  const int64_t g = blockIdx.x / nb;
+  const int64_t e0 = (blockIdx.x % nb) * kRChunk;
+  const int64_t layer = g / a.H;
+  for (int i = threadIdx.x; i < kRankBins; i += kRT) h[i] = 0u;
   __syncthreads();
-  long long nz = 0;
-  for (int64_t e = threadIdx.x; e < (int64_t)H * width; e += kBT) nz |= (sc[e] != 0.0) ? 1 : 0;
-  nz = block_sum(nz, red);
-  for (int hh = 0; hh < H; ++hh) {
-    long long c = 0;
-    for (int64_t e = threadIdx.x; e < width; e += kBT) c += keep[(size_t)hh * width + e];
-    c = block_sum(c, red);
-    if (threadIdx.x == 0) cnt[hh] = (int)c;
+  const int sh = rank_shift(pass), top = sh + rank_bits(pass);
+  const uint32_t mask = (1u << rank_bits(pass)) - 1u;
+  const uint32_t pre = a.prefix[layer];
+  const float* zg = a.z + (size_t)g * a.N + a.s_cnt;
+  for (int t = 0; t < kRPer; ++t) {
+    const int64_t e = e0 + t * kRT + threadIdx.x;
+    if (e < a.width) {
+      const uint32_t key = __float_as_uint(zg[e]);
+      if (top == 32 || (key >> top) == (pre >> top)) atomicAdd(&h[(key >> sh) & mask], 1u);
+    }
   }
-  if (threadIdx.x == 0) anynz = nz != 0;
   __syncthreads();
-  if (threadIdx.x != 0) return;
+  uint32_t* gh = a.hist + (size_t)layer * kRankBins;
+  for (int i = threadIdx.x; i < kRankBins; i += kRT)
+    if (h[i]) atomicAdd(&gh[i], h[i]);
+}
+
+// One block per layer: the digit of the bin that holds the need-th largest
+// matching entry, and what remains to take inside it; clears the histogram
+// for the next pass.
+__global__ __launch_bounds__(kRT) void rank_scan_kernel(AllocArgs a, int pass) {
+  __shared__ uint32_t wsum[kRT / 64];
+  const int64_t layer = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int nb = 1 << rank_bits(pass), per = nb / kRT;
+  uint32_t* gh = a.hist + (size_t)layer * kRankBins;
+  const int64_t need = a.need[layer];
+  const uint32_t pre = a.prefix[layer];
+  // thread t owns bins nb-1-per*t down to nb-per*(t+1), highest first
+  uint32_t c[kRankBins / kRT];
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < kRankBins / kRT; ++i) {
+    c[i] = i < per ? gh[nb - 1 - per * t - i] : 0u;
+    s += c[i];
+  }
+  uint32_t inc = s;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_up(inc, off);
+    if (lane >= off) inc += v;
+  }
+  if (lane == 63) wsum[wv] = inc;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int w = 0; w < wv; ++w) before += wsum[w];
+  const int64_t excl = (int64_t)before + inc - s;
+  if (excl < need && need <= excl + (int64_t)s) {
+    int64_t run = excl;
+    for (int i = 0; i < per; ++i) {
+      if (run + c[i] >= need) {
+        a.prefix[layer] = pre | ((uint32_t)(nb - 1 - per * t - i) << rank_shift(pass));
+        a.need[layer] = need - run;
+        break;
+      }
+      run += c[i];
+    }
+  }
+  for (int i = 0; i < per; ++i) gh[nb - 1 - per * t - i] = 0u;
+}
+
+// Per head: entries above the layer's threshold, equal to it, and nonzero.
+__global__ __launch_bounds__(kRT) void rank_count_kernel(AllocArgs a) {
+  __shared__ uint32_t red[3][kRT / 64];
+  const int64_t nb = (a.width + kRChunk - 1) / kRChunk;
+  const int64_t g = blockIdx.x / nb;
+  const int64_t e0 = (blockIdx.x % nb) * kRChunk;
+  const uint32_t T = a.prefix[g / a.H];
+  const float* zg = a.z + (size_t)g * a.N + a.s_cnt;
+  uint32_t v[3] = {0u, 0u, 0u};
+  for (int t = 0; t < kRPer; ++t) {
+    const int64_t e = e0 + t * kRT + threadIdx.x;
+    if (e < a.width) {
+      const uint32_t key = __float_as_uint(zg[e]);
+      v[0] += key > T;
+      v[1] += key == T;
+      v[2] += key != 0u;
+    }
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v[k] += __shfl_xor(v[k], off);
+    if (lane == 0) red[k][wv] = v[k];
+  }
+  __syncthreads();
+  if (threadIdx.x < 3) {
+    uint32_t tot = 0;
+    for (int w = 0; w < kRT / 64; ++w) tot += red[threadIdx.x][w];
+    if (tot) atomicAdd(&a.counts[(size_t)g * 3 + threadIdx.x], tot);
+  }
+}
+
+// One thread per layer: g_h from the counts and the threshold's remaining
+// take, then Equation 5.
+__global__ void rank_alloc_kernel(AllocArgs a) {
+  const int64_t layer = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (layer >= a.L) return;
+  const int H = a.H;
+  const uint32_t* cnt = a.counts + (size_t)layer * H * 3;
+  bool anynz = false;
+  for (int hh = 0; hh < H; ++hh) anynz |= cnt[3 * hh + 2] != 0u;
   const int64_t U = a.U;
   int64_t floor_sum = 0;
+  int64_t need = a.need[layer];
   for (int hh = 0; hh < H; ++hh) {
-    if (!anynz) cnt[hh] = (int)U;
-    floor_sum += (cnt[hh] + U) / 2;
+    const int64_t take = need < (int64_t)cnt[3 * hh + 1] ? need : (int64_t)cnt[3 * hh + 1];
+    need -= take;
+    const int64_t gh = anynz ? (int64_t)cnt[3 * hh] + take : U;
+    floor_sum += (gh + U) / 2;
   }
   int64_t R = (int64_t)H * U - floor_sum;
+  need = a.need[layer];
   for (int hh = 0; hh < H; ++hh) {
-    const int64_t twice = cnt[hh] + U;
+    const int64_t take = need < (int64_t)cnt[3 * hh + 1] ? need : (int64_t)cnt[3 * hh + 1];
+    need -= take;
+    const int64_t gh = anynz ? (int64_t)cnt[3 * hh] + take : U;
+    const int64_t twice = gh + U;
     int64_t u = twice / 2;
     if ((twice & 1) && R > 0) {
       u += 1;
@@ -297,7 +412,7 @@ __global__ __launch_bounds__(kBT) void alloc_kernel(AllocArgs a) {
     }
     const size_t o = (size_t)layer * H + hh;
     a.capacity[o] = (int32_t)(a.P + u);
-    if (a.g_count) a.g_count[o] = cnt[hh];
+    if (a.g_count) a.g_count[o] = (int32_t)gh;
   }
 }
 
@@ -332,7 +447,18 @@ hipError_t launch_attn(const AttnArgs& a, int d, int phase, hipStream_t stream) 
 }
 
 hipError_t launch_alloc(const AllocArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(alloc_kernel, dim3((unsigned)a.L), dim3(kBT), 0, stream, a);
+  const int64_t nb = (a.width + kRChunk - 1) / kRChunk;
+  const int64_t blocks = a.G * nb;
+  if (blocks < 1 || blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  int64_t init = a.L * kRankBins;
+  if (a.G * 3 > init) init = a.G * 3;
+  hipLaunchKernelGGL(rank_init_kernel, dim3((unsigned)((init + 255) / 256)), dim3(256), 0, stream, a);
+  for (int pass = 0; pass < 3; ++pass) {
+    hipLaunchKernelGGL(rank_hist_kernel, dim3((unsigned)blocks), dim3(kRT), 0, stream, a, pass);
+    hipLaunchKernelGGL(rank_scan_kernel, dim3((unsigned)a.L), dim3(kRT), 0, stream, a, pass);
+  }
+  hipLaunchKernelGGL(rank_count_kernel, dim3((unsigned)blocks), dim3(kRT), 0, stream, a);
+  hipLaunchKernelGGL(rank_alloc_kernel, dim3((unsigned)((a.L + 63) / 64)), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

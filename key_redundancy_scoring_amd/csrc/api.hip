@@ -93,8 +93,8 @@ size_t alloc_ws(const twinkv_params* p, int32_t H, int32_t Gq, int32_t W, int64_
   const size_t G = (size_t)p->G, N = (size_t)p->N;
   return align_up(G * s.nchunk * s.Q * 2 * sizeof(double)) + align_up(G * s.Q * 2 * sizeof(double)) +
          align_up(G * N * sizeof(double)) + align_up(G * N * sizeof(float)) +
-         align_up(G * (size_t)s.width * sizeof(double)) + align_up(G * (size_t)s.width) +
-         align_up((size_t)s.L * sizeof(int32_t));
+         align_up((size_t)s.L * 2048 * sizeof(uint32_t)) + align_up((size_t)s.L * sizeof(uint32_t)) +
+         align_up((size_t)s.L * sizeof(int64_t)) + align_up(G * 3 * sizeof(uint32_t));
 }
 
 int record(hipEvent_t* marks, int k, hipStream_t s) {
@@ -289,9 +289,11 @@ int twinkv_allocate(const twinkv_params* p, int32_t H, int32_t Gq, int32_t W, in
   aa.mz = cv.take<double>(G * sh.Q * 2);
   aa.agg = cv.take<double>(G * N);
   float* zbuf = cv.take<float>(G * N);
-  aa.pool_score = cv.take<double>(G * (size_t)sh.width);
-  uint8_t* pool_keep = cv.take<uint8_t>(G * (size_t)sh.width);
-  int32_t* pool_cap = cv.take<int32_t>((size_t)sh.L);
+  AllocArgs al{};
+  al.hist = cv.take<uint32_t>((size_t)sh.L * 2048);
+  al.prefix = cv.take<uint32_t>((size_t)sh.L);
+  al.need = cv.take<int64_t>((size_t)sh.L);
+  al.counts = cv.take<uint32_t>(G * 3);
   aa.keys = static_cast<const uint16_t*>(keys);
   aa.queries = static_cast<const uint16_t*>(queries);
   aa.G = p->G;
@@ -315,27 +317,15 @@ int twinkv_allocate(const twinkv_params* p, int32_t H, int32_t Gq, int32_t W, in
     // no unprotected slots: allocation is skipped and every head keeps B
     TRY_HIP(launch_fill_capacity(capacity, g_count, p->G, (int32_t)B, stream));
   } else {
-    TRY_HIP(launch_fill_capacity(pool_cap, nullptr, sh.L, (int32_t)(H * sh.U), stream));
-    SelectArgs sa{};
-    sa.score = aa.pool_score;
-    sa.energy = aa.pool_score;  // equal scores fall through to the pool index: head, then position
-    sa.capacity = pool_cap;
-    sa.keep = pool_keep;
-    sa.kept_idx = nullptr;
-    sa.kept_idx_len = 0;
-    sa.G = sh.L;
-    sa.N = (int64_t)H * sh.width;
-    sa.sink = 0;
-    sa.recent = 0;
-    TRY_HIP(launch_select(sa, stream));
-    AllocArgs al{};
+    al.z = aa.z;
+    al.G = p->G;
+    al.N = p->N;
     al.L = sh.L;
     al.H = H;
+    al.s_cnt = sh.s_cnt;
     al.width = sh.width;
     al.U = sh.U;
     al.P = sh.P;
-    al.pool_keep = pool_keep;
-    al.pool_score = aa.pool_score;
     al.capacity = capacity;
     al.g_count = g_count;
     TRY_HIP(launch_alloc(al, stream));

@@ -80,16 +80,18 @@ struct AttnArgs {
   double* mz;               // [G][Gq*W][2] per query (max, normaliser)
   double* agg;              // [G][N] attention summed over queries, averaged over query heads
   float* z;                 // [G][N] pooled fp32 scores
-  double* pool_score;       // [G][N - s - r] unprotected scores, head after head
   int64_t s_cnt, r_cnt;     // protected leading / trailing positions
 };
 struct AllocArgs {
-  int64_t L;                // layers
+  const float* z;           // [G][N] pooled fp32 scores
+  int64_t G, N, L;          // heads, positions, layers
   int32_t H;                // KV heads per layer
-  int64_t width;            // unprotected positions per head
+  int64_t s_cnt, width;     // unprotected positions s_cnt .. s_cnt + width - 1 of a head
   int64_t U, P;
-  const uint8_t* pool_keep; // [L][H * width] selected pool entries
-  const double* pool_score; // [L][H * width]
+  uint32_t* hist;           // [L][2048] digit histograms (workspace)
+  uint32_t* prefix;         // [L] threshold bits (workspace)
+  int64_t* need;            // [L] entries still to take at the threshold (workspace)
+  uint32_t* counts;         // [G][3] above, at the threshold, nonzero (workspace)
   int32_t* capacity;        // [G] out
   int32_t* g_count;         // [G] out, may be null
 };

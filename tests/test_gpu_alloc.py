@@ -119,3 +119,21 @@ def test_allocation_fullsize_llama32_1b_32k():
     s, r = O.protected_counts(B, cfg.sink, cfg.recent)
     _check_budget(res, H, B, s + r, B - s - r, "alloc 32k")
     _check_layers(K, Q, res, H, N, B, cfg.sink, cfg.recent, [0, G // H - 1], "alloc 32k")
+
+
+def test_allocation_tied_scores():
+    """Every head of a layer holds one key repeated N times: the causal
+    softmax is uniform, so every head has the same z at every position and
+    the whole ranking is decided by the tie rule (lower head, then lower
+    position).  A second layer mixes tied and random heads."""
+    cfg = get_config(2)
+    N, H = 600, 4
+    K, Q = _inputs(cfg, 2 * H, N)
+    K[:H] = K[0, 0]
+    K[H:H + 2] = K[H, 0]
+    B = O.uniform_budget(N, 0.5)
+    res = krs.allocate(_up(K), _up(Q), H, B, cfg.sink, cfg.recent)
+    torch.cuda.synchronize()
+    _check_layers(K, Q, res, H, N, B, cfg.sink, cfg.recent, [0, 1], "tied")
+    s, r = O.protected_counts(B, cfg.sink, cfg.recent)
+    _check_budget(res, H, B, s + r, B - s - r, "tied")
