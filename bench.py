@@ -187,7 +187,8 @@ def main():
         sl = krs.select(r["score"], r["energy"], caps, cfg.sink, cfg.recent, out=sel_out, events=ev_sel,
                         offsets=offsets)
         sel_out.update({"keep": sl["keep"], "kept_idx": sl["kept_idx"]})
-        rp = krs.repair(K, sl["keep"], cfg.tau, cfg.window, cfg.sink, cfg.recent, out=rep_out, ws=r_ws, events=ev_r)
+        rp = krs.repair(K, sl["keep"], cfg.tau, cfg.window, cfg.sink, cfg.recent, prior=r, out=rep_out, ws=r_ws,
+                        events=ev_r)
         r_ws = rp["ws"]
         rep_out.update({k: rp[k] for k in ("keep", "best_sim", "best_idx", "n_orphans", "n_donors", "n_swaps",
                                            "pairs")})
@@ -291,6 +292,11 @@ def main():
     exec_tflops = dense / (gram_ms * 1e-3) / 1e12
     mean_cap = float(np.mean(cap_list))
     rgram = restricted_gram_flops(N, mean_cap, d, G)
+    # rows the restricted sweep visits: those whose unrestricted best twin
+    # (the prior from the score pass) was not retained
+    bi = s_out["best_idx"].long()
+    reused = (bi < 0) | torch.gather(sel_out["keep"], 1, bi.clamp(min=0)).bool()
+    swept_frac = 1.0 - reused.float().mean().item()
     norms_bytes = G * N * (4 * d + 20)
 
     traffic = None
@@ -328,7 +334,8 @@ def main():
                       "repair_norms": r_norms_ms, "repair_compact": r_compact_ms, "repair_gram": r_gram_ms,
                       "repair_swap": r_swap_ms},
         "phase_rates": {"norms_energy_GBs": norms_bytes / (norms_ms * 1e-3) / 1e9,
-                        "repair_gram_dense_tflops": rgram / (r_gram_ms * 1e-3) / 1e12},
+                        "repair_gram_dense_tflops": rgram * swept_frac / (r_gram_ms * 1e-3) / 1e12,
+                        "repair_rows_swept_frac": swept_frac},
         "gather_kv": {"ms": gather_ms, "rows": gather_rows, "algorithmic_bytes": gather_bytes,
                       "GBs": gather_bytes / (gather_ms * 1e-3) / 1e9,
                       "frac_hbm": gather_bytes / (gather_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},

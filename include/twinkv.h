@@ -175,14 +175,26 @@ int twinkv_select(const twinkv_params* params, const double* score, const double
  *   swap_pairs: int32 [G][N/2][2]: (O[k], D[k]) for k < m, then (-1, -1)
  *     (m <= N/2 always: m <= min(N - K, K)).
  * keys: bf16 [G][N][d]; keep_in: uint8 [G][N].
+ * prior_sim, prior_idx (double / int32 [G][N], both NULL or both given): the
+ *   unrestricted best twin (best_sim, best_idx) that twinkv_score wrote for the
+ *   same keys, window and tau.  Where prior_idx[g][i] is retained (or is -1:
+ *   no nonlocal position exists), it is b_i(S0) with its position, since the
+ *   lowest position attaining the maximum over all nonlocal j is then in S0;
+ *   those rows are copied and only the others are swept.  The outputs are the
+ *   same as without a prior, except that such a row reports the prior's
+ *   (exact fp64) choice where two positions' fp32 similarities are within
+ *   rounding of each other.  An index outside [0, N) counts as not retained;
+ *   any other inconsistent prior gives wrong results, never an access outside
+ *   the stated sizes.  Both NULL: every row is swept.
  * Phases for `marks`: 0 = norms, 1 = compaction of S0 (retained positions and a
- * contiguous copy of their keys), 2 = restricted Gram and fixup,
- * 3 = classification, ranking and swap.
+ * contiguous copy of their keys) and of the rows to sweep, 2 = restricted
+ * Gram and fixup, 3 = classification, ranking and swap.
  */
 int twinkv_repair(const twinkv_params* params, const void* keys, const uint8_t* keep_in,
-                  uint8_t* keep_out, double* best_sim, int32_t* best_idx, int32_t* n_orphans,
-                  int32_t* n_donors, int32_t* n_swaps, int32_t* swap_pairs, void* workspace,
-                  size_t workspace_bytes, hipStream_t stream, hipEvent_t* marks);
+                  const double* prior_sim, const int32_t* prior_idx, uint8_t* keep_out,
+                  double* best_sim, int32_t* best_idx, int32_t* n_orphans, int32_t* n_donors,
+                  int32_t* n_swaps, int32_t* swap_pairs, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream, hipEvent_t* marks);
 
 /*
  * twinkv_variant_score - selection keys of a score variant for twinkv_select,

@@ -69,7 +69,7 @@ def load():
     lib.twinkv_score.restype = ctypes.c_int
     lib.twinkv_select.argtypes = [P, vp, vp, vp, vp, vp, i64, vp, sz, vp, vp]
     lib.twinkv_select.restype = ctypes.c_int
-    lib.twinkv_repair.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    lib.twinkv_repair.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.twinkv_repair.restype = ctypes.c_int
     lib.twinkv_gather_kv.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp, vp]
     lib.twinkv_gather_kv.restype = ctypes.c_int
@@ -285,10 +285,13 @@ def select(score_t, energy_t, capacity, sink=4, recent=64, out=None, events=None
     return {"keep": keep, "kept_idx": kept, "offsets": off, "capacity": capacity}
 
 
-def repair(keys, keep_in, tau, window, sink=4, recent=64, out=None, ws=None, events=None):
+def repair(keys, keep_in, tau, window, sink=4, recent=64, prior=None, out=None, ws=None, events=None):
     """One-shot orphan/donor repair of the retained masks ``keep_in`` (uint8
-    [G][N]).  Returns keep (S1), best_sim, best_idx, n_orphans, n_donors,
-    n_swaps and pairs ([G][N//2][2], -1 padded)."""
+    [G][N]).  ``prior``: optionally the result of ``score`` on the same keys,
+    window and tau (its best_sim and best_idx); rows whose unrestricted best
+    twin is retained then take it instead of being swept again.  Returns keep
+    (S1), best_sim, best_idx, n_orphans, n_donors, n_swaps and pairs
+    ([G][N//2][2], -1 padded)."""
     lib = load()
     keys = _as_bf16_bits(keys, "keys")
     G, N, d = keys.shape
@@ -297,6 +300,13 @@ def repair(keys, keep_in, tau, window, sink=4, recent=64, out=None, ws=None, eve
             or keep_in.device != dev:
         raise ValueError("keep_in must be contiguous uint8 [G][N] on the keys' device")
     p = params(G, N, d, tau, window, sink, recent)
+    ps = pi = ctypes.c_void_p(0)
+    if prior is not None:
+        psim, pidx = prior["best_sim"], prior["best_idx"]
+        for t, dt, nm in ((psim, torch.float64, "best_sim"), (pidx, torch.int32, "best_idx")):
+            if t.dtype != dt or tuple(t.shape) != (G, N) or not t.is_contiguous() or t.device != dev:
+                raise ValueError(f"prior {nm} must be contiguous {dt} [G][N] on the keys' device")
+        ps, pi = _ptr(psim), _ptr(pidx)
     out = {} if out is None else out
     o = {
         "keep": _need(out.get("keep"), (G, N), torch.uint8, dev, "keep"),
@@ -310,7 +320,7 @@ def repair(keys, keep_in, tau, window, sink=4, recent=64, out=None, ws=None, eve
     nb = workspace_bytes(OP_REPAIR, p)
     ws = _workspace(ws, nb, dev)
     wp, wn = _ws_ptr(ws)
-    st = lib.twinkv_repair(ctypes.byref(p), _ptr(keys), _ptr(keep_in), _ptr(o["keep"]), _ptr(o["best_sim"]),
+    st = lib.twinkv_repair(ctypes.byref(p), _ptr(keys), _ptr(keep_in), ps, pi, _ptr(o["keep"]), _ptr(o["best_sim"]),
                            _ptr(o["best_idx"]), _ptr(o["n_orphans"]), _ptr(o["n_donors"]), _ptr(o["n_swaps"]),
                            _ptr(o["pairs"]) if N >= 2 else ctypes.c_void_p(0), wp, wn, _stream(),
                            _marks(events, REPAIR_PHASES))

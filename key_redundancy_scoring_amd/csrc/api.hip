@@ -54,8 +54,9 @@ size_t score_ws(const twinkv_params* p) {
 
 size_t repair_ws(const twinkv_params* p) {
   const size_t n = (size_t)p->G * (size_t)p->N;
-  return align_up(n * sizeof(double)) + align_up(n * sizeof(float)) + align_up(n * sizeof(int32_t)) +
-         align_up((size_t)p->G * sizeof(int32_t)) + 2 * (align_up(n * sizeof(uint64_t)) + align_up(n * sizeof(int32_t))) +
+  return align_up(n * sizeof(double)) + align_up(n * sizeof(float)) + 2 * align_up(n * sizeof(int32_t)) +
+         2 * align_up((size_t)p->G * sizeof(int32_t)) +
+         2 * (align_up(n * sizeof(uint64_t)) + align_up(n * sizeof(int32_t))) +
          align_up(n * (size_t)p->d * sizeof(uint16_t)) + align_up(n * sizeof(float));
 }
 
@@ -334,13 +335,14 @@ int twinkv_allocate(const twinkv_params* p, int32_t H, int32_t Gq, int32_t W, in
   return TWINKV_OK;
 }
 
-int twinkv_repair(const twinkv_params* p, const void* keys, const uint8_t* keep_in, uint8_t* keep_out,
-                  double* best_sim, int32_t* best_idx, int32_t* n_orphans, int32_t* n_donors, int32_t* n_swaps,
-                  int32_t* swap_pairs, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                  hipEvent_t* marks) {
+int twinkv_repair(const twinkv_params* p, const void* keys, const uint8_t* keep_in, const double* prior_sim,
+                  const int32_t* prior_idx, uint8_t* keep_out, double* best_sim, int32_t* best_idx,
+                  int32_t* n_orphans, int32_t* n_donors, int32_t* n_swaps, int32_t* swap_pairs, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream, hipEvent_t* marks) {
   TRY(check_params(p));
   if (!keys || !keep_in || !keep_out || !best_sim || !best_idx || !n_orphans || !n_donors || !n_swaps)
     return TWINKV_ERR_ARG;
+  if ((prior_sim == nullptr) != (prior_idx == nullptr)) return TWINKV_ERR_ARG;
   if (p->N >= 2 && !swap_pairs) return TWINKV_ERR_ARG;
   if (!aligned16(keys)) return TWINKV_ERR_ARG;
   if (keep_in == keep_out) return TWINKV_ERR_ARG;
@@ -354,6 +356,8 @@ int twinkv_repair(const twinkv_params* p, const void* keys, const uint8_t* keep_
   float* rinv = cv.take<float>(n);
   int32_t* pos = cv.take<int32_t>(n);
   int32_t* ncols = cv.take<int32_t>((size_t)p->G);
+  int32_t* row_pos = cv.take<int32_t>(n);
+  int32_t* nrows = cv.take<int32_t>((size_t)p->G);
   uint64_t* keys_a = cv.take<uint64_t>(n);
   int32_t* idx_a = cv.take<int32_t>(n);
   uint64_t* keys_b = cv.take<uint64_t>(n);
@@ -367,6 +371,7 @@ int twinkv_repair(const twinkv_params* p, const void* keys, const uint8_t* keep_
   TRY(record(marks, 1, stream));
   TRY_HIP(launch_compact(keep_in, p->G, p->N, pos, ncols, stream));
   TRY_HIP(launch_gather(kin, rinv, pos, ncols, p->G, p->N, p->d, ckeys, crinv, stream));
+  TRY_HIP(launch_rows(keep_in, prior_sim, prior_idx, p->G, p->N, row_pos, nrows, best_sim, best_idx, stream));
   TRY(record(marks, 2, stream));
   GramArgs ga{};
   ga.keys = kin;
@@ -375,6 +380,8 @@ int twinkv_repair(const twinkv_params* p, const void* keys, const uint8_t* keep_
   ga.col_rinv = crinv;
   ga.col_pos = pos;
   ga.ncols = ncols;
+  ga.row_pos = row_pos;
+  ga.nrows = nrows;
   ga.G = p->G;
   ga.N = p->N;
   ga.d = p->d;

@@ -5,7 +5,9 @@
 //     Frequency Corrections ...", section 3.2), score mode only;
 //   * the best nonlocal twin b_i = max sim(i,j) over the same j and its lowest
 //     position a_i; in repair mode the columns are the retained set S0, which
-//     gives b_i(S0) of Eq. 4 ("TwinKV ...", section 3.4);
+//     gives b_i(S0) of Eq. 4 ("TwinKV ...", section 3.4), for the rows of a
+//     given list (all rows, or those whose unrestricted best twin was not
+//     retained);
 // and, in score mode, the discounted score e_i * ln((N+1)/(c_i+1)) ("Small
 // Frequency Corrections ...", section 3.2).  The N x N similarity matrix is
 // never written anywhere.
@@ -197,6 +199,12 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
   const float* crinv_g = a.col_rinv + (size_t)g * N;
   const int32_t* cpos_g = (MODE == GRAM_REPAIR) ? a.col_pos + (size_t)g * N : nullptr;
   const int ncols = (MODE == GRAM_REPAIR) ? a.ncols[g] : (int)N;
+  // repair mode sweeps the rows listed in row_pos (ascending positions); row
+  // r of the list is position row_of(r), clamped to the last listed row
+  const int nrows = (MODE == GRAM_REPAIR) ? a.nrows[g] : (int)N;
+  if ((int64_t)rb * ROWS >= nrows) return;  // the whole workgroup, before any barrier
+  const int32_t* rpos_g = (MODE == GRAM_REPAIR) ? a.row_pos + (size_t)g * N : nullptr;
+  auto row_of = [&](int r) TWINKV_INLINE { return (MODE == GRAM_REPAIR) ? rpos_g[r < nrows ? r : nrows - 1] : r; };
 
   // ---- row keys as MFMA B operands, row state
   bf16x8 brow[RB][KS];
@@ -204,14 +212,15 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
   int btile[RB], cnt[RB];
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
-    const int i = row0 + 32 * b + lrow;
+    const int r = row0 + 32 * b + lrow;
+    const int i = row_of(r);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       uint4 v = {0u, 0u, 0u, 0u};
-      if (i < N) v = Kg[(size_t)i * CH + 2 * s + h];
+      if (r < nrows) v = Kg[(size_t)i * CH + 2 * s + h];
       brow[b][s] = __builtin_bit_cast(bf16x8, v);
     }
-    thr[b] = (i < N && MODE == GRAM_SCORE) ? (float)(a.tau * sqrt(a.nsq[(size_t)g * N + i])) : __builtin_inff();
+    thr[b] = (r < nrows && MODE == GRAM_SCORE) ? (float)(a.tau * sqrt(a.nsq[(size_t)g * N + i])) : __builtin_inff();
     best[b] = -__builtin_inff();
     btile[b] = -1;
     cnt[b] = 0;
@@ -285,6 +294,9 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
       rv[4 * gq + 3] = r4.w;
     }
   };
+  // first and last row position of the wave (wave-uniform)
+  const int rlo = __builtin_amdgcn_readfirstlane(row_of(row0));
+  const int rhi = __builtin_amdgcn_readfirstlane(row_of(row0 + RB * 32 - 1));
   // Bit tt set: some block of the wave's rows meets the |i-j| <= w band or
   // the ragged tail in tile tt of stage st (wave-uniform).
   auto masked_tiles = [&](const Stage<D, SC>& sb, int st) TWINKV_INLINE {
@@ -300,7 +312,7 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
         pmin = c0;
         pmax = c0 + 31;
       }
-      const bool mk = (c0 + 31 >= ncols) || (pmin <= row0 + RB * 32 - 1 + w && pmax >= row0 - w);
+      const bool mk = (c0 + 31 >= ncols) || (pmin <= rhi + w && pmax >= rlo - w);
       bits |= (unsigned)mk << tt;
     }
     return bits;
@@ -457,7 +469,7 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
       for (int b = 0; b < RB; ++b) {
         f32x16 y;
         mfma_block(Am, b, y);
-        const int i = row0 + 32 * b + lrow;
+        const int i = row_of(row0 + 32 * b + lrow);
         float yy[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -487,8 +499,8 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
   // decisions, so the row's result needs no further merge.
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
-    const int i = row0 + 32 * b + lrow;
-    const bool row_ok = i < N;
+    const int i = row_of(row0 + 32 * b + lrow);
+    const bool row_ok = row0 + 32 * b + lrow < nrows;
     double bb = -1.0;
     int aa = -1;
     const double ni = row_ok ? a.nsq[(size_t)g * N + i] : 0.0;

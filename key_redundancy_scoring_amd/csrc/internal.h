@@ -17,6 +17,8 @@ struct GramArgs {
   const float* col_rinv;     // 1/||k|| in fp32 of each column [G][N] (0 for a zero key)
   const int32_t* col_pos;    // repair: original position of each compacted column, ascending [G][N]
   const int32_t* ncols;      // repair: number of retained positions per head [G]
+  const int32_t* row_pos;    // repair: positions of the rows to sweep, ascending [G][N]
+  const int32_t* nrows;      // repair: number of rows to sweep per head [G]
   const double* energy;   // score: ||v||^2 [G][N]
   int64_t G, N;
   int32_t d, window;
@@ -54,6 +56,11 @@ hipError_t launch_variant(const int32_t* count, const double* energy, const int3
 
 hipError_t launch_compact(const uint8_t* keep_in, int64_t G, int64_t N, int32_t* pos, int32_t* ncols,
                           hipStream_t stream);
+// The rows the restricted sweep must visit (all rows without a prior); rows
+// whose unrestricted best twin is retained or absent take it as b_i(S0).
+hipError_t launch_rows(const uint8_t* keep_in, const double* prior_sim, const int32_t* prior_idx, int64_t G,
+                       int64_t N, int32_t* row_pos, int32_t* nrows, double* best_sim, int32_t* best_idx,
+                       hipStream_t stream);
 // Copy the retained keys and their inverse norms into column order.
 hipError_t launch_gather(const uint16_t* keys, const float* rinv, const int32_t* pos, const int32_t* ncols, int64_t G,
                          int64_t N, int d, uint16_t* ckeys, float* crinv, hipStream_t stream);

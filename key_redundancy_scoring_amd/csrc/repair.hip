@@ -42,6 +42,43 @@ __global__ __launch_bounds__(kBT) void compact_kernel(const uint8_t* __restrict_
   if (threadIdx.x == 0) ncols[g] = base;
 }
 
+// The rows of the restricted sweep.  The prior (prior_sim, prior_idx) is the
+// unrestricted best nonlocal twin of each position, from the score pass over
+// the same keys and window.  If it is retained, it is also b_i(S0) with its
+// position: the lowest position attaining the maximum over all nonlocal j
+// lies in S0, so it attains the maximum over S0's nonlocal j, and no lower
+// position of S0 does.  If there is no nonlocal j at all (prior_idx = -1),
+// S0 has none either.  Those rows take the prior and are not swept; the
+// others are listed in ascending order.  Without a prior every row is
+// listed.  A prior index outside [0, N) is treated as not retained.
+__global__ __launch_bounds__(kBT) void rows_kernel(const uint8_t* __restrict__ keep_in,
+                                                   const double* __restrict__ prior_sim,
+                                                   const int32_t* __restrict__ prior_idx, int64_t N,
+                                                   int32_t* __restrict__ row_pos, int32_t* __restrict__ nrows,
+                                                   double* __restrict__ best_sim, int32_t* __restrict__ best_idx) {
+  __shared__ ScanSmem sc;
+  const int64_t g = blockIdx.x;
+  const size_t o = (size_t)g * N;
+  int base = 0;
+  for (int64_t b = 0; b < N; b += kBT) {
+    const int64_t i = b + threadIdx.x;
+    bool f = i < N;
+    if (f && prior_idx) {
+      const int32_t j = prior_idx[o + i];
+      if (j < 0 || (j < N && keep_in[o + j] != 0)) {
+        f = false;
+        best_sim[o + i] = prior_sim[o + i];
+        best_idx[o + i] = j;
+      }
+    }
+    int tot = 0;
+    const int r = block_scan_flag(f, sc, &tot);
+    if (f) row_pos[o + base + r] = (int32_t)i;
+    base += tot;
+  }
+  if (threadIdx.x == 0) nrows[g] = base;
+}
+
 // Copy retained key rows (and their inverse norms) into column order, so the
 // restricted Gram sweep streams contiguous rows: ckeys[g][k] = keys[g][pos[g][k]]
 // for k < ncols[g].  One 16-byte chunk per thread and step.
@@ -171,6 +208,14 @@ __global__ __launch_bounds__(kBT) void swap_kernel(SwapArgs a) {
 hipError_t launch_compact(const uint8_t* keep_in, int64_t G, int64_t N, int32_t* pos, int32_t* ncols,
                           hipStream_t stream) {
   hipLaunchKernelGGL(compact_kernel, dim3((unsigned)G), dim3(kBT), 0, stream, keep_in, N, pos, ncols);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows(const uint8_t* keep_in, const double* prior_sim, const int32_t* prior_idx, int64_t G,
+                       int64_t N, int32_t* row_pos, int32_t* nrows, double* best_sim, int32_t* best_idx,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL(rows_kernel, dim3((unsigned)G), dim3(kBT), 0, stream, keep_in, prior_sim, prior_idx, N, row_pos,
+                     nrows, best_sim, best_idx);
   return hipGetLastError();
 }
 

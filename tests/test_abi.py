@@ -94,14 +94,17 @@ def test_select_validation():
 
 def test_repair_validation():
     lib = krs.load()
-    call = lambda p, keep_out=FAKE, pairs=FAKE, ws=FAKE, nb=1 << 30: lib.twinkv_repair(  # noqa: E731
-        ctypes.byref(p), FAKE, FAKE, keep_out, FAKE, FAKE, FAKE, FAKE, FAKE, pairs, ws, nb, None, None)
+    call = lambda p, keep_out=FAKE, pairs=FAKE, ws=FAKE, nb=1 << 30, ps=None, pi=None: lib.twinkv_repair(  # noqa: E731
+        ctypes.byref(p), FAKE, FAKE, ps, pi, keep_out, FAKE, FAKE, FAKE, FAKE, FAKE, pairs, ws, nb, None, None)
     good = krs.params(2, 100, 128, 0.9, 8)
     assert call(krs.params(2, 100, 32, 0.9, 8)) == L.ERR_UNSUPPORTED
     assert call(good, keep_out=None) == L.ERR_ARG
     assert call(good, keep_out=FAKE) == L.ERR_ARG  # keep_out aliases keep_in
     assert call(good, keep_out=ctypes.c_void_p(0x200000), pairs=None) == L.ERR_ARG
     assert call(good, keep_out=ctypes.c_void_p(0x200000), nb=100) == L.ERR_WORKSPACE
+    # a prior needs both its similarity and its index
+    assert call(good, keep_out=ctypes.c_void_p(0x200000), ps=FAKE) == L.ERR_ARG
+    assert call(good, keep_out=ctypes.c_void_p(0x200000), pi=FAKE) == L.ERR_ARG
 
 
 def test_params_struct_layout():

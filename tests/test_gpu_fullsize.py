@@ -191,7 +191,10 @@ def _score_select(cfg, K, V, caps, repair_selected):
     off = krs.capacity_offsets(caps, cfg.N)
     sel = krs.select(res["score"], res["energy"], torch.tensor(caps, dtype=torch.int32, device=_dev()), cfg.sink,
                      cfg.recent, offsets=off)
-    rep = krs.repair(tk, sel["keep"], cfg.tau, cfg.window, cfg.sink, cfg.recent) if repair_selected else None
+    # the repair of the selection reuses the score pass's best twins, as a
+    # score -> select -> repair step does
+    rep = krs.repair(tk, sel["keep"], cfg.tau, cfg.window, cfg.sink, cfg.recent,
+                     prior=res) if repair_selected else None
     torch.cuda.synchronize()
     return res, sel, rep
 

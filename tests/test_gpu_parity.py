@@ -42,9 +42,11 @@ def _run_score_select_repair(K, V, cfg, caps, do_repair_on_select=False, tag="")
     res = krs.score(tk, tv, cfg.tau, cfg.window, cfg.sink, cfg.recent, omega=True)
     sel = krs.select(res["score"], res["energy"], torch.tensor(caps, dtype=torch.int32, device=_dev()),
                      cfg.sink, cfg.recent)
-    rep_res = None
+    rep_res = rep_pr = None
     if do_repair_on_select:
         rep_res = krs.repair(tk, sel["keep"], cfg.tau, cfg.window, cfg.sink, cfg.recent)
+        # the same repair, reusing the score pass's unrestricted best twins
+        rep_pr = krs.repair(tk, sel["keep"], cfg.tau, cfg.window, cfg.sink, cfg.recent, prior=res)
     torch.cuda.synchronize()
     keep = sel["keep"].cpu().numpy()
     kept = sel["kept_idx"].cpu().numpy()
@@ -66,10 +68,11 @@ def _run_score_select_repair(K, V, cfg, caps, do_repair_on_select=False, tag="")
         r["select_exact"] = exact
         if rep_res is not None and exact:
             rref = PR.repair_reference(K[g], okeep, cfg.tau, cfg.window, cfg.sink, cfg.recent)
-            rg = {k: rep_res[k][g].cpu().numpy() for k in ("keep", "n_orphans", "n_donors", "n_swaps", "pairs")}
-            rg["best"] = rep_res["best_sim"][g].cpu().numpy()
-            rg["arg"] = rep_res["best_idx"][g].cpu().numpy()
-            r["repair"] = PR.compare_repair(rg, rref, okeep, cfg.tau, tag=f"{tag} head {g} repair")
+            for name, rr in (("repair", rep_res), ("repair with prior", rep_pr)):
+                rg = {k: rr[k][g].cpu().numpy() for k in ("keep", "n_orphans", "n_donors", "n_swaps", "pairs")}
+                rg["best"] = rr["best_sim"][g].cpu().numpy()
+                rg["arg"] = rr["best_idx"][g].cpu().numpy()
+                r[name] = PR.compare_repair(rg, rref, okeep, cfg.tau, tag=f"{tag} head {g} {name}")
         reports.append(r)
     _say(f"[{tag}] ok", reports[:2])
     return res, sel, reports
@@ -229,3 +232,37 @@ def test_deterministic_repeat():
     torch.cuda.synchronize()
     for k in ("count", "best_sim", "best_idx", "energy", "score", "omega"):
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("cfg_id,G,N,removal", [(2, 4, 2500, 0.5), (3, 3, 1700, 0.3), (2, 2, 900, 0.9)])
+def test_repair_prior_matches_full_sweep(cfg_id, G, N, removal):
+    """Repair with the score pass's best twins as the prior against the full
+    restricted sweep, on the GPU: the same b(S0) and position wherever the
+    two sweeps' fp32 screens are not within rounding of a tie, and then the
+    same orphans, donors, pairs and S1.  Heads with a random retained set and
+    with the score-ranked one."""
+    cfg = get_config(cfg_id)
+    K, V, _ = make_heads(cfg, heads=range(G), N=N)
+    tk, tv = _up(K), _up(V)
+    res = krs.score(tk, tv, cfg.tau, cfg.window, cfg.sink, cfg.recent)
+    cap = O.uniform_budget(N, removal)
+    sel = krs.select(res["score"], res["energy"], torch.full((G,), cap, dtype=torch.int32, device=_dev()),
+                     cfg.sink, cfg.recent)
+    rnd = torch.from_numpy(np.stack([gumbel_retained(cfg, g, N=N, keep=cap) for g in range(G)])).to(_dev())
+    for name, keep in (("selected", sel["keep"]), ("random", rnd)):
+        full = krs.repair(tk, keep, cfg.tau, cfg.window, cfg.sink, cfg.recent)
+        pr = krs.repair(tk, keep, cfg.tau, cfg.window, cfg.sink, cfg.recent, prior=res)
+        torch.cuda.synchronize()
+        fa, pa = full["best_idx"].cpu().numpy(), pr["best_idx"].cpu().numpy()
+        fb, pb = full["best_sim"].cpu().numpy(), pr["best_sim"].cpu().numpy()
+        diff = fa != pa
+        # a different choice only between positions whose similarities agree
+        # to within the fp32 screen's rounding
+        np.testing.assert_allclose(pb[diff], fb[diff], rtol=0, atol=1e-5, err_msg=f"{name} near-tie rows")
+        np.testing.assert_array_equal(pb[~diff], fb[~diff], err_msg=f"{name} b(S0)")
+        if not diff.any():
+            for k in ("keep", "n_orphans", "n_donors", "n_swaps", "pairs"):
+                assert torch.equal(full[k], pr[k]), f"{name} {k}"
+        reused = (pa >= 0) & np.take_along_axis(keep.cpu().numpy(), np.maximum(res["best_idx"].cpu().numpy(), 0),
+                                                1).astype(bool)
+        _say(f"[prior {name} cfg{cfg_id}] rows reused {reused.mean():.3f}, differing choices {int(diff.sum())}")
