@@ -37,9 +37,17 @@
 namespace twinkv {
 namespace {
 
-constexpr int kAT = 256;            // threads per attention block = keys per block
-constexpr int kKG = 4;              // key groups of 16 per wave: 64 keys per wave
+constexpr int kAT = 256;            // keys per attention block
 constexpr int kQG = kMaxQueries / 16;
+
+// Waves per attention block and key groups of 16 per wave (256 keys per
+// block either way): a wave's key operands, widened to fp64, take
+// 2*(d/4)*KG registers per lane, so d = 128 spreads a block over more waves.
+template <int D>
+struct AttnShape {
+  static constexpr int KG = D == 64 ? 4 : 2;
+  static constexpr int WAVES = kAT / (16 * KG);
+};
 
 typedef double v4d __attribute__((ext_vector_type(4)));
 
@@ -72,20 +80,24 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 // The logits of one block: 256 keys of one head against its Q = Gq*W
 // observing queries, on the fp64 matrix cores (v_mfma_f64_16x16x4f64: lane l
 // supplies A[l%16][l/16] and B[l/16][l%16] and holds D[l/16 + 4r][l%16],
-// r = 0..3, as measured on gfx950).  A tile is 16 queries x 16 keys; a wave owns 4 key groups (64
-// keys) and walks the query groups.  The feature index of step s in lane
+// r = 0..3, as measured on gfx950).  A tile is 16 queries x 16 keys; a wave
+// owns KG key groups (16*KG keys) and walks the query groups.  The feature
+// index of step s in lane
 // group k is (d/4)k + s, so a lane's operands are contiguous slices of a row.
 // The bf16 products are exact in fp64; only the sums round.  The queries are
 // staged once per block in LDS as fp32 (exact), in operand order, so each
 // wave reads one contiguous 1 KiB per four steps; the keys stay in registers
 // as fp32.  Both are widened to fp64 at the matrix core's input.
 template <int D, int PHASE>
-__global__ __launch_bounds__(kAT) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * AttnShape<D>::WAVES) void attn_kernel(AttnArgs a) {
   constexpr int KS = D / 4;  // k-steps per tile
   constexpr int C8 = D / 8;  // 16-byte chunks per bf16 row
+  constexpr int kKG = AttnShape<D>::KG;
+  constexpr int NW = AttnShape<D>::WAVES;
+  constexpr int NT = 64 * NW;
   __shared__ float4 qa[kQG * (KS / 4) * 64];
-  __shared__ double pm[kAT / 64][kMaxQueries];
-  __shared__ double pz[kAT / 64][kMaxQueries];
+  __shared__ double pm[NW][kMaxQueries];
+  __shared__ double pz[NW][kMaxQueries];
   __shared__ double2 smr[kMaxQueries];  // (max, 1 / normaliser)
 
   const int64_t g = blockIdx.x / a.nchunk;
@@ -97,7 +109,7 @@ __global__ __launch_bounds__(kAT) void attn_kernel(AttnArgs a) {
 
   {
     const uint4* qsrc = reinterpret_cast<const uint4*>(a.queries) + (size_t)g * Q * C8;
-    for (int e = tid; e < nqg * 16 * C8; e += kAT) {
+    for (int e = tid; e < nqg * 16 * C8; e += NT) {
       const int qq = e / C8, c = e % C8;
       const uint4 u = qq < Q ? qsrc[(size_t)qq * C8 + c] : make_uint4(0u, 0u, 0u, 0u);
       const int f0 = 8 * c;
@@ -106,7 +118,7 @@ __global__ __launch_bounds__(kAT) void attn_kernel(AttnArgs a) {
       dst[64] = make_float4(bf_lo(u.z), bf_hi(u.z), bf_lo(u.w), bf_hi(u.w));
     }
     if (PHASE == 2) {
-      for (int q = tid; q < nqg * 16; q += kAT) {
+      for (int q = tid; q < nqg * 16; q += NT) {
         double2 v = make_double2(0.0, 0.0);
         if (q < Q) {
           v.x = a.mz[((size_t)g * Q + q) * 2];
@@ -118,7 +130,7 @@ __global__ __launch_bounds__(kAT) void attn_kernel(AttnArgs a) {
   }
 
   const int64_t N = a.N;
-  const int64_t j0 = chunk * kAT + wv * 64 + (lane & 15);
+  const int64_t j0 = chunk * kAT + wv * (16 * kKG) + (lane & 15);
   float kb[kKG][KS];
 #pragma unroll
   for (int kg = 0; kg < kKG; ++kg) {
@@ -192,14 +204,14 @@ __global__ __launch_bounds__(kAT) void attn_kernel(AttnArgs a) {
 
   if (PHASE == 1) {
     __syncthreads();
-    for (int q = tid; q < Q; q += kAT) {
+    for (int q = tid; q < Q; q += NT) {
       double m = -__builtin_inf();
 #pragma unroll
-      for (int w = 0; w < kAT / 64; ++w) m = fmax(m, pm[w][q]);
+      for (int w = 0; w < NW; ++w) m = fmax(m, pm[w][q]);
       double z = 0.0;
       if (m > -__builtin_inf()) {
 #pragma unroll
-        for (int w = 0; w < kAT / 64; ++w)
+        for (int w = 0; w < NW; ++w)
           if (pm[w][q] > -__builtin_inf()) z += pz[w][q] * exp(pm[w][q] - m);
       }
       double* dst = a.part + (((size_t)g * a.nchunk + chunk) * Q + q) * 2;
@@ -430,14 +442,18 @@ hipError_t launch_attn(const AttnArgs& a, int d, int phase, hipStream_t stream) 
   const int64_t blocks = a.G * a.nchunk;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (phase == 1) {
-    if (d == 64) hipLaunchKernelGGL((attn_kernel<64, 1>), dim3((unsigned)blocks), dim3(kAT), 0, stream, a);
-    else hipLaunchKernelGGL((attn_kernel<128, 1>), dim3((unsigned)blocks), dim3(kAT), 0, stream, a);
+    if (d == 64)
+      hipLaunchKernelGGL((attn_kernel<64, 1>), dim3((unsigned)blocks), dim3(64 * AttnShape<64>::WAVES), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_kernel<128, 1>), dim3((unsigned)blocks), dim3(64 * AttnShape<128>::WAVES), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)a.G), dim3(kMaxQueries), 0, stream, a);
   } else {
-    if (d == 64) hipLaunchKernelGGL((attn_kernel<64, 2>), dim3((unsigned)blocks), dim3(kAT), 0, stream, a);
-    else hipLaunchKernelGGL((attn_kernel<128, 2>), dim3((unsigned)blocks), dim3(kAT), 0, stream, a);
+    if (d == 64)
+      hipLaunchKernelGGL((attn_kernel<64, 2>), dim3((unsigned)blocks), dim3(64 * AttnShape<64>::WAVES), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_kernel<128, 2>), dim3((unsigned)blocks), dim3(64 * AttnShape<128>::WAVES), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nb = (a.N + kAT - 1) / kAT;
