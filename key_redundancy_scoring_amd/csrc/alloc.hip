@@ -31,7 +31,6 @@
 // them would take Gq*W*N*8 bytes per head, while recomputing is matrix-core
 // work that runs beside the exponentials on the vector units.
 
-#include "blockops.h"
 #include "internal.h"
 
 namespace twinkv {
