@@ -69,7 +69,8 @@ def _check_budget(res, H, B, P, U, tag):
     assert np.all(cap >= P + U // 2), f"{tag} capacity floor"
 
 
-@pytest.mark.parametrize("cfg_id,L,H,N", [(2, 2, 8, 1500), (3, 1, 8, 700), (2, 1, 4, 300)])
+@pytest.mark.parametrize("cfg_id,L,H,N", [(2, 2, 8, 1500), (3, 1, 8, 700), (2, 1, 4, 300), (3, 2, 4, 3000),
+                                          (2, 6, 1, 900)])
 def test_allocation_small(cfg_id, L, H, N):
     cfg = get_config(cfg_id)
     G = L * H

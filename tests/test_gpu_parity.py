@@ -266,3 +266,26 @@ def test_repair_prior_matches_full_sweep(cfg_id, G, N, removal):
         reused = (pa >= 0) & np.take_along_axis(keep.cpu().numpy(), np.maximum(res["best_idx"].cpu().numpy(), 0),
                                                 1).astype(bool)
         _say(f"[prior {name} cfg{cfg_id}] rows reused {reused.mean():.3f}, differing choices {int(diff.sum())}")
+
+
+def test_repair_prior_out_of_range_indices_are_swept():
+    """Prior indices outside [0, N) count as not retained: those rows are
+    swept, so the result equals the full restricted sweep."""
+    cfg = get_config(2)
+    G, N = 2, 1200
+    K, V, _ = make_heads(cfg, heads=range(G), N=N)
+    tk, tv = _up(K), _up(V)
+    res = krs.score(tk, tv, cfg.tau, cfg.window, cfg.sink, cfg.recent)
+    keep = torch.from_numpy(np.stack([gumbel_retained(cfg, g, N=N) for g in range(G)])).to(_dev())
+    bad = {"best_sim": res["best_sim"].clone(), "best_idx": res["best_idx"].clone()}
+    bad["best_idx"][:, ::3] = N + 5
+    bad["best_idx"][:, 1::7] = 2 ** 31 - 1
+    full = krs.repair(tk, keep, cfg.tau, cfg.window, cfg.sink, cfg.recent)
+    pr = krs.repair(tk, keep, cfg.tau, cfg.window, cfg.sink, cfg.recent, prior=bad)
+    torch.cuda.synchronize()
+    rows = np.zeros((G, N), bool)
+    rows[:, ::3] = True
+    rows[:, 1::7] = True
+    fa, pa = full["best_idx"].cpu().numpy(), pr["best_idx"].cpu().numpy()
+    np.testing.assert_array_equal(pa[rows], fa[rows])
+    np.testing.assert_array_equal(pr["best_sim"].cpu().numpy()[rows], full["best_sim"].cpu().numpy()[rows])
