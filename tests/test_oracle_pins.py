@@ -694,3 +694,36 @@ def test_count_stats_planted_fraction():
     assert sum(st["hist"]) == st["n"] == int((~prot).sum())
     assert st["kept"] == cap - int(prot.sum())
     assert st["added"] == st["removed"]  # both selections keep the same number
+
+
+def test_restricted_twin_is_the_unrestricted_one_when_retained():
+    """[P1] section 3.4, Eq. 4: b_i(S0) is a maximum over the retained nonlocal
+    positions.  When the lowest position attaining the maximum over all
+    nonlocal positions is retained, it is also b_i(S0)'s position, with the
+    same value; otherwise b_i(S0) is no larger; with no nonlocal position at
+    all both are -1.  Checked with the pure-Python brute force (exact ties
+    planted by duplicated keys) and against the oracle's restricted twin."""
+    rng = np.random.default_rng(41)
+    reused = 0
+    for trial in range(24):
+        N = int(rng.integers(2, 40))
+        w = int(rng.integers(0, 4))
+        K = rng.integers(-3, 4, size=(N, 4)).astype(float)
+        if N > 4:
+            K[rng.integers(0, N, 3)] = K[rng.integers(0, N)]  # exact ties
+        S0 = rng.random(N) < 0.5
+        allr = brute.twin_stats(K.tolist(), 0.9, w)
+        subr = brute.twin_stats(K.tolist(), 0.9, w, allowed=S0.tolist())
+        ob, oa = O.best_surviving_twin(K, S0.astype(np.uint8), w)
+        for i in range(N):
+            _, fb, fa = allr[i]
+            _, sb, sa = subr[i]
+            assert (sb, sa) == (ob[i], oa[i]) or (math.isclose(sb, ob[i], rel_tol=1e-15) and sa == oa[i])
+            if fa < 0:
+                assert sa < 0 and sb == -1.0
+            elif S0[fa]:
+                assert (sa, sb) == (fa, fb)
+                reused += 1
+            else:
+                assert sb <= fb
+    assert reused > 50
