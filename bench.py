@@ -53,13 +53,13 @@ GRAM_SOURCE = os.path.join(ROOT, "key_redundancy_scoring_amd", "csrc", "gram.hip
 # reading for a plain device copy of known size; keyed by the sha256 of the
 # Gram source the counters were taken on.
 MEASURED_TRAFFIC: dict = {
-    "6ca4a78868c037eb4fddc843f89a7ee4003f8f23040fcc78887dc10b5feae16c": {
+    "680f5d554ebe43420a408def26b87c5bd186ea80e77fc6f2ec06652c50ab6fe9": {
         "workload": (128, 32768, 64),
-        # FETCH_SIZE 2274917.9 KiB x 1.99994 (a 1 GiB copy reads 524302.7 KiB),
-        # WRITE_SIZE 98304.0 KiB x 1.0 (the same copy writes 1048576 KiB)
-        "fetch_bytes": 4658901754,
-        "write_bytes": 100663296,
-        "bytes_per_launch": 4759565050,
+        # FETCH_SIZE 1851610.9 KiB x 1.99994 (a 1 GiB copy reads 524302.8 KiB),
+        # WRITE_SIZE 114688.0 KiB x 1.0 (the same copy writes 1048576 KiB)
+        "fetch_bytes": 3791991758,
+        "write_bytes": 117440512,
+        "bytes_per_launch": 3909432270,
     },
 }
 

@@ -13,7 +13,9 @@
 // never written anywhere.
 //
 // Mapping onto gfx950:
-//   * A workgroup of WAVES waves owns WAVES*RB*32 consecutive rows of one head;
+//   * A workgroup of WAVES waves owns WAVES*RB*32 consecutive rows of one head
+//     (in repair mode, consecutive entries of the row list: their positions
+//     ascend, and the band test below uses the first and last of a wave);
 //     each wave owns RB blocks of 32 rows whose bf16 keys stay in VGPRs as
 //     MFMA B operands for the whole sweep.  Two workgroups share a CU, so one
 //     workgroup's prologue and fp64 fixup overlap the other's sweep.
@@ -220,7 +222,9 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
       if (r < nrows) v = Kg[(size_t)i * CH + 2 * s + h];
       brow[b][s] = __builtin_bit_cast(bf16x8, v);
     }
-    thr[b] = (r < nrows && MODE == GRAM_SCORE) ? (float)(a.tau * sqrt(a.nsq[(size_t)g * N + i])) : __builtin_inff();
+    // + 0.0f turns a -0 threshold (tau = -0, or a zero key with tau < 0) into +0
+    thr[b] = (r < nrows && MODE == GRAM_SCORE) ? (float)(a.tau * sqrt(a.nsq[(size_t)g * N + i])) + 0.0f
+                                               : __builtin_inff();
     best[b] = -__builtin_inff();
     btile[b] = -1;
     cnt[b] = 0;
@@ -325,11 +329,13 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
     return bits;
   };
   // count of y > tau*||k_i|| over the 16 values of a block
+  // (y > thr read off the sign bit of thr - y: there are no NaNs, thr is
+  // never -0, and a zero difference is +0; no compare-to-carry hazards)
   auto count16 = [&](const f32x16& y, int b) TWINKV_INLINE {
-    int c = 0;
+    uint32_t c = 0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) c += (y[r] > thr[b]) ? 1 : 0;
-    cnt[b] += c;
+    for (int r = 0; r < 16; ++r) c += __float_as_uint(thr[b] - y[r]) >> 31;
+    cnt[b] += (int)c;
   };
   auto mfma_block = [&](const bf16x8 (&A)[KS], int b, f32x16& acc) TWINKV_INLINE {
     acc = (f32x16){};
