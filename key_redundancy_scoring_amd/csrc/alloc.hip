@@ -40,11 +40,14 @@ constexpr int kAT = 256;            // keys per attention block
 constexpr int kQG = kMaxQueries / 16;
 
 // Waves per attention block and key groups of 16 per wave (256 keys per
-// block either way): a wave's key operands, widened to fp64, take
-// 2*(d/4)*KG registers per lane, so d = 128 spreads a block over more waves.
-template <int D>
+// block either way).  A wave's key operands, widened to fp64, take
+// 2*(d/4)*KG registers per lane and its two accumulator sets 16*KG; the
+// d = 64 statistics pass keeps four key groups (each query operand read
+// feeds four MFMAs), the other passes take two so they keep two waves per
+// SIMD.
+template <int D, int PHASE>
 struct AttnShape {
-  static constexpr int KG = D == 64 ? 4 : 2;
+  static constexpr int KG = (D == 64 && PHASE == 1) ? 4 : 2;
   static constexpr int WAVES = kAT / (16 * KG);
 };
 
@@ -88,11 +91,11 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 // wave reads one contiguous 1 KiB per four steps; the keys stay in registers
 // as fp32.  Both are widened to fp64 at the matrix core's input.
 template <int D, int PHASE>
-__global__ __launch_bounds__(64 * AttnShape<D>::WAVES) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__((64 * AttnShape<D, PHASE>::WAVES)) void attn_kernel(AttnArgs a) {
   constexpr int KS = D / 4;  // k-steps per tile
   constexpr int C8 = D / 8;  // 16-byte chunks per bf16 row
-  constexpr int kKG = AttnShape<D>::KG;
-  constexpr int NW = AttnShape<D>::WAVES;
+  constexpr int kKG = AttnShape<D, PHASE>::KG;
+  constexpr int NW = AttnShape<D, PHASE>::WAVES;
   constexpr int NT = 64 * NW;
   __shared__ float4 qa[kQG * (KS / 4) * 64];
   __shared__ double pm[NW][kMaxQueries];
@@ -151,9 +154,8 @@ __global__ __launch_bounds__(64 * AttnShape<D>::WAVES) void attn_kernel(AttnArgs
 
   const double scale = a.inv_sqrt_d;
   double agg[kKG] = {};
-#pragma unroll 1
-  for (int qg = 0; qg < nqg; ++qg) {
-    v4d acc[kKG];
+  // The logits of query group qg into acc.
+  auto mfma_group = [&](int qg, v4d(&acc)[kKG]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kg = 0; kg < kKG; ++kg) acc[kg] = v4d{0.0, 0.0, 0.0, 0.0};
     const float4* ap = qa + qg * (KS / 4) * 64 + lane;
@@ -168,6 +170,12 @@ __global__ __launch_bounds__(64 * AttnShape<D>::WAVES) void attn_kernel(AttnArgs
           acc[kg] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)af[u], (double)kb[kg][4 * s4 + u], acc[kg], 0, 0, 0);
       }
     }
+  };
+  // The softmax work of query group qg, without branches: a masked logit
+  // enters the exponential as -inf, which gives 0.  Phase 1 leaves each
+  // row's (max, sum) in pmv/pzv for store().
+  double pmv[4], pzv[4];
+  auto epilogue = [&](int qg, const v4d(&acc)[kKG]) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int q = qg * 16 + kq + 4 * r;
@@ -187,18 +195,62 @@ __global__ __launch_bounds__(64 * AttnShape<D>::WAVES) void attn_kernel(AttnArgs
         m = row16_max(m);
         double z = 0.0;
 #pragma unroll
-        for (int kg = 0; kg < kKG; ++kg) z += ok[kg] ? exp(v[kg] - m) : 0.0;
-        z = row16_sum(z);
-        if ((lane & 15) == 0 && q < Q) {
-          pm[wv][q] = m;
-          pz[wv][q] = z;
-        }
+        for (int kg = 0; kg < kKG; ++kg) z += exp(ok[kg] ? v[kg] - m : -__builtin_inf());
+        pmv[r] = m;
+        pzv[r] = row16_sum(z);
       } else {
         const double2 mr = smr[q];
 #pragma unroll
-        for (int kg = 0; kg < kKG; ++kg) agg[kg] += ok[kg] ? exp(v[kg] - mr.x) * mr.y : 0.0;
+        for (int kg = 0; kg < kKG; ++kg) agg[kg] += exp(ok[kg] ? v[kg] - mr.x : -__builtin_inf()) * mr.y;
       }
     }
+  };
+  auto store = [&](int qg) __attribute__((always_inline)) {
+    if (PHASE == 1 && (lane & 15) == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int q = qg * 16 + kq + 4 * r;
+        if (q < Q) {
+          pm[wv][q] = pmv[r];
+          pz[wv][q] = pzv[r];
+        }
+      }
+    }
+  };
+  // Spread one query group's epilogue over the next group's MFMAs.
+  auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < KS * kKG; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // up to six VALU
+    }
+  };
+  // Software pipeline over the query groups: the MFMAs of group qg+1 run
+  // while the vector units do group qg's exponentials.
+  v4d accA[kKG], accB[kKG];
+  mfma_group(0, accA);
+  int qg = 0;
+#pragma unroll 1
+  for (; qg + 2 < nqg; qg += 2) {
+    mfma_group(qg + 1, accB);
+    epilogue(qg, accA);
+    interleave();
+    store(qg);
+    mfma_group(qg + 2, accA);
+    epilogue(qg + 1, accB);
+    interleave();
+    store(qg + 1);
+  }
+  if (qg + 1 < nqg) {
+    mfma_group(qg + 1, accB);
+    epilogue(qg, accA);
+    interleave();
+    store(qg);
+    epilogue(qg + 1, accB);
+    store(qg + 1);
+  } else {
+    epilogue(qg, accA);
+    store(qg);
   }
 
   if (PHASE == 1) {
@@ -442,17 +494,17 @@ hipError_t launch_attn(const AttnArgs& a, int d, int phase, hipStream_t stream) 
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (phase == 1) {
     if (d == 64)
-      hipLaunchKernelGGL((attn_kernel<64, 1>), dim3((unsigned)blocks), dim3(64 * AttnShape<64>::WAVES), 0, stream, a);
+      hipLaunchKernelGGL((attn_kernel<64, 1>), dim3((unsigned)blocks), dim3(64 * AttnShape<64, 1>::WAVES), 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_kernel<128, 1>), dim3((unsigned)blocks), dim3(64 * AttnShape<128>::WAVES), 0, stream, a);
+      hipLaunchKernelGGL((attn_kernel<128, 1>), dim3((unsigned)blocks), dim3(64 * AttnShape<128, 1>::WAVES), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)a.G), dim3(kMaxQueries), 0, stream, a);
   } else {
     if (d == 64)
-      hipLaunchKernelGGL((attn_kernel<64, 2>), dim3((unsigned)blocks), dim3(64 * AttnShape<64>::WAVES), 0, stream, a);
+      hipLaunchKernelGGL((attn_kernel<64, 2>), dim3((unsigned)blocks), dim3(64 * AttnShape<64, 2>::WAVES), 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_kernel<128, 2>), dim3((unsigned)blocks), dim3(64 * AttnShape<128>::WAVES), 0, stream, a);
+      hipLaunchKernelGGL((attn_kernel<128, 2>), dim3((unsigned)blocks), dim3(64 * AttnShape<128, 2>::WAVES), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nb = (a.N + kAT - 1) / kAT;
