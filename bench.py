@@ -55,11 +55,11 @@ GRAM_SOURCE = os.path.join(ROOT, "key_redundancy_scoring_amd", "csrc", "gram.hip
 MEASURED_TRAFFIC: dict = {
     "680f5d554ebe43420a408def26b87c5bd186ea80e77fc6f2ec06652c50ab6fe9": {
         "workload": (128, 32768, 64),
-        # FETCH_SIZE 1851610.9 KiB x 1.99994 (a 1 GiB copy reads 524302.8 KiB),
+        # FETCH_SIZE 1829741.7 KiB x 1.99994 (a 1 GiB copy reads 524302.6 KiB),
         # WRITE_SIZE 114688.0 KiB x 1.0 (the same copy writes 1048576 KiB)
-        "fetch_bytes": 3791991758,
+        "fetch_bytes": 3747206537,
         "write_bytes": 117440512,
-        "bytes_per_launch": 3909432270,
+        "bytes_per_launch": 3864647049,
     },
 }
 
