@@ -175,7 +175,34 @@ def _oracle_head_checks(K, V, g, cfg, res, sel, rep, cap, tag):
         rg["arg"] = rep["best_idx"][g].cpu().numpy()
         r["repair"] = PR.compare_repair(rg, rref, okeep, cfg.tau, tag=f"{tag} head {g} repair")
     r["select_exact"] = exact
+    r["variants"] = _variant_checks(ref, cfg, cap, tag=f"{tag} head {g}")
     _say(f"[{tag}] head {g} whole-head parity ok: {r}")
+
+
+def _variant_checks(ref, cfg, cap, tag):
+    """Score variants of one whole head at full size: the oracle's counts and
+    energies go through the GPU's variant keys and selection; the keys match
+    the oracle's variant_scores and the kept sets its select_head (rarity
+    also with the standalone score's ceil budget)."""
+    N = cfg.N
+    c = torch.from_numpy(ref["count"].astype(np.int32)[None]).to(_dev())
+    e = torch.from_numpy(np.ascontiguousarray(ref["energy"])[None]).to(_dev())
+    r = cfg.removal if cfg.removal is not None else 0.5
+    out = {}
+    for name, cp in (("value", cap), ("rarity", cap), ("rarity", O.ceil_budget(N, r))):
+        v = krs.variant_score(c, e, name)
+        sel = krs.select(v["score"], v["tie"], [cp], cfg.sink, cfg.recent)
+        torch.cuda.synchronize()
+        rs, rt = O.variant_scores(ref["energy"], ref["count"], N, name)
+        np.testing.assert_allclose(v["score"][0].cpu().numpy(), rs, rtol=1e-13, atol=0, err_msg=f"{tag} {name}")
+        np.testing.assert_array_equal(v["tie"][0].cpu().numpy(), rt, err_msg=f"{tag} {name} tie")
+        okeep, _ = O.select_head(rs, rt, cp, cfg.sink, cfg.recent)
+        if PR.boundary_gap(rs, rt, cp, cfg.sink, cfg.recent) >= PR.BOUNDARY_GAP:
+            np.testing.assert_array_equal(sel["keep"][0].cpu().numpy(), okeep, err_msg=f"{tag} {name} keep")
+            out[f"{name}@{cp}"] = "exact"
+        else:
+            out[f"{name}@{cp}"] = "boundary near-tie"
+    return out
 
 
 def _row_checks(K, V, g, cfg, res, tag):
