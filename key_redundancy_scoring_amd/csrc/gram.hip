@@ -518,9 +518,15 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
     const bool look = row_ok && btile[b] >= 0 && best[b] >= other - margin;
     const bool look_o = __shfl_xor((int)look, 32) != 0;
     const int tile_o = __shfl_xor(btile[b], 32);
+    // the halves of the row to examine, the same in both lanes of the row:
+    // the first pass takes each row's lower looking half, the second (rare)
+    // its upper half when both halves are within the margin
+    const bool look0 = (h == 0) ? look : look_o;
+    const bool look1 = (h == 1) ? look : look_o;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const bool lk = (h == p) ? look : look_o;  // same in both lanes of the row
+    for (int pass = 0; pass < 2; ++pass) {
+      const int p = (pass == 0 && look0) ? 0 : 1;
+      const bool lk = pass == 0 ? (look0 || look1) : (look0 && look1);
       const int tp = (h == p) ? btile[b] : tile_o;
       if (__ballot(lk) == 0ull) continue;
       if (lk) {
