@@ -53,13 +53,13 @@ GRAM_SOURCE = os.path.join(ROOT, "key_redundancy_scoring_amd", "csrc", "gram.hip
 # reading for a plain device copy of known size; keyed by the sha256 of the
 # Gram source the counters were taken on.
 MEASURED_TRAFFIC: dict = {
-    "680f5d554ebe43420a408def26b87c5bd186ea80e77fc6f2ec06652c50ab6fe9": {
+    "639850450b44a375f1d8554cfdccb6574cc929bdca6363b42037f96cba6f0daf": {
         "workload": (128, 32768, 64),
-        # FETCH_SIZE 1829741.7 KiB x 1.99994 (a 1 GiB copy reads 524302.6 KiB),
+        # FETCH_SIZE 1899539.3 KiB x 1.99994 (a 1 GiB copy reads 524302.8 KiB),
         # WRITE_SIZE 114688.0 KiB x 1.0 (the same copy writes 1048576 KiB)
-        "fetch_bytes": 3747206537,
+        "fetch_bytes": 3890146941,
         "write_bytes": 117440512,
-        "bytes_per_launch": 3864647049,
+        "bytes_per_launch": 4007587453,
     },
 }
 
