@@ -24,8 +24,9 @@ d-length dot product (2d flop) per unordered nonlocal pair, while `gram`
 also gives the dense-equivalent rate (both orders of every pair, the work the
 sweep executes).  `traffic` is the HBM traffic per launch measured with
 rocprofv3 counters for the current Gram source (null when the source has
-changed since).  `cpu_baseline` times the fp64 oracle's score stage on the
-host over row blocks of the same workload, for about 12 s.
+changed since).  `cpu_baseline` times the fp64 oracle's whole step (score,
+select, repair of the selection) on whole heads of the same workload, on the
+host, for about `--cpu-seconds` (at least one head).
 """
 from __future__ import annotations
 
