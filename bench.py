@@ -48,19 +48,21 @@ PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU (pub
 PEAK_HBM_GBS = 8000.0
 PEAK_FP64_TFLOPS = 78.6
 GRAM_SOURCE = os.path.join(ROOT, "key_redundancy_scoring_amd", "csrc", "gram.hip")
+# launch shape of the score-mode sweep per head dim, as the kernel trace names it
+SCORE_SHAPE = {64: "GramShape<64, 4, 4, 256, 2>", 128: "GramShape<128, 2, 4, 128, 2>"}
 
 # HBM traffic of one score-mode Gram launch on the default workload, from
 # rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the counters'
 # reading for a plain device copy of known size; keyed by the sha256 of the
 # Gram source the counters were taken on.
 MEASURED_TRAFFIC: dict = {
-    "639850450b44a375f1d8554cfdccb6574cc929bdca6363b42037f96cba6f0daf": {
+    "8e228c205b2f4f0945eb331799a250fe6168612366bc8425fb4467f59077fa47": {
         "workload": (128, 32768, 64),
-        # FETCH_SIZE 1899539.3 KiB x 1.99994 (a 1 GiB copy reads 524302.8 KiB),
+        # FETCH_SIZE 1875232.2 KiB x 1.99994 (a 1 GiB copy reads 524302.6 KiB),
         # WRITE_SIZE 114688.0 KiB x 1.0 (the same copy writes 1048576 KiB)
-        "fetch_bytes": 3890146941,
+        "fetch_bytes": 3840368895,
         "write_bytes": 117440512,
-        "bytes_per_launch": 4007587453,
+        "bytes_per_launch": 3957809407,
     },
 }
 
@@ -325,7 +327,7 @@ def main():
                    "recent": cfg.recent, "mean_capacity": mean_cap, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "kernel": f"gram_kernel<{d}, score>", "algorithmic_flop_per_launch": alg,
+                     "kernel": f"gram_kernel<{SCORE_SHAPE[d]}, score>", "algorithmic_flop_per_launch": alg,
                      "avg_launch_ms": gram_ms},
         "gram": {"dense_equiv_tflops": exec_tflops, "mfma_frac_dense_equiv": exec_tflops / PEAK_BF16_TFLOPS,
                  "keys_per_s": G * N / (gram_ms * 1e-3), "ms": gram_ms},

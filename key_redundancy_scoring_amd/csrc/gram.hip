@@ -17,8 +17,9 @@
 //     (in repair mode, consecutive entries of the row list: their positions
 //     ascend, and the band test below uses the first and last of a wave);
 //     each wave owns RB blocks of 32 rows whose bf16 keys stay in VGPRs as
-//     MFMA B operands for the whole sweep.  Two workgroups share a CU, so one
-//     workgroup's prologue and fp64 fixup overlap the other's sweep.
+//     MFMA B operands for the whole sweep.  Two workgroups share a CU (three
+//     in the repair shape), so one workgroup's prologue and fp64 fixup
+//     overlap another's sweep.
 //   * Column keys stream HBM/L2 -> LDS in stages of SC columns with
 //     global_load_lds (no VGPR round trip), into two LDS buffers: stage s+1
 //     is in flight while stage s is computed, and the one wait per stage sits
@@ -88,21 +89,25 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int D>
-struct Shape;
-template <>
-struct Shape<64> {
-  static constexpr int RB = TWINKV_GRAM64_RB, WAVES = TWINKV_GRAM64_WAVES, SC = TWINKV_GRAM64_SC;
+// Launch shape of the sweep: head dim, row blocks of 32 per wave, waves per
+// workgroup, columns per LDS stage, and waves per SIMD the registers are
+// budgeted for (two stage buffers of SC columns per workgroup must fit the
+// CU's LDS that many times over).
+template <int D_, int RB_, int WAVES_, int SC_, int OCC_>
+struct GramShape {
+  static constexpr int D = D_, RB = RB_, WAVES = WAVES_, SC = SC_, OCC = OCC_;
+  static constexpr int ROWS = WAVES * RB * 32;
 };
-template <>
-struct Shape<128> {
-  static constexpr int RB = TWINKV_GRAM128_RB, WAVES = TWINKV_GRAM128_WAVES, SC = TWINKV_GRAM128_SC;
-};
-
-template <int D>
-constexpr int rows_per_wg() {
-  return Shape<D>::WAVES * Shape<D>::RB * 32;
-}
+// score mode at d = 64: four row blocks per wave, so each staged column
+// feeds 128 rows of the wave; about 240 VGPRs, two waves per SIMD
+using Shape64 = GramShape<64, TWINKV_GRAM64_RB, TWINKV_GRAM64_WAVES, TWINKV_GRAM64_SC, 2>;
+// repair mode at d = 64: two row blocks per wave at three waves per SIMD (at
+// most 168 VGPRs).  The restricted sweep covers only the retained columns,
+// often a few thousand, so the per-workgroup tail (masked tiles, fixup) weighs
+// more, and a third wave per SIMD hides it better than the column reuse of
+// four row blocks pays
+using Shape64Short = GramShape<64, 2, 4, 128, 3>;
+using Shape128 = GramShape<128, TWINKV_GRAM128_RB, TWINKV_GRAM128_WAVES, TWINKV_GRAM128_SC, 2>;
 
 // vmcnt(0), other counters untouched (gfx9 s_waitcnt encoding)
 constexpr unsigned kWaitVm0 = 0x0F70;
@@ -161,13 +166,14 @@ __device__ __forceinline__ int swz(int c) {
 // column offset (within a 32-column tile) of accumulator r in half-wave h
 __device__ __forceinline__ int tile_col(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-template <int D, int MODE>
-__global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gram_kernel(GramArgs a) {
-  constexpr int RB = Shape<D>::RB;
-  constexpr int WAVES = Shape<D>::WAVES;
-  constexpr int SC = Shape<D>::SC;
+template <class S, int MODE>
+__global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a) {
+  constexpr int D = S::D;
+  constexpr int RB = S::RB;
+  constexpr int WAVES = S::WAVES;
+  constexpr int SC = S::SC;
   constexpr int NT = 64 * WAVES;   // threads
-  constexpr int ROWS = rows_per_wg<D>();
+  constexpr int ROWS = S::ROWS;
   constexpr int CH = D / 8;        // 16-byte chunks per key row
   constexpr int KS = D / 16;       // MFMA k-steps
   constexpr int LOADS = SC * CH / NT;
@@ -619,22 +625,22 @@ __global__ __launch_bounds__(64 * Shape<D>::WAVES, 8 / Shape<D>::WAVES) void gra
   }
 }
 
-template <int D, int MODE>
+template <class S, int MODE>
 hipError_t launch_dm(const GramArgs& a, hipStream_t stream) {
-  constexpr int ROWS = rows_per_wg<D>();
-  const int64_t bph = (a.N + ROWS - 1) / ROWS;
+  const int64_t bph = (a.N + S::ROWS - 1) / S::ROWS;
   const int64_t total = a.G * bph;
   const int64_t grid = 8 * ((total + 7) / 8);
   if (grid > INT_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gram_kernel<D, MODE>), dim3((unsigned)grid), dim3(64 * Shape<D>::WAVES), 0, stream, a);
+  hipLaunchKernelGGL((gram_kernel<S, MODE>), dim3((unsigned)grid), dim3(64 * S::WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gram(const GramArgs& a, int mode, hipStream_t stream) {
-  if (a.d == 64) return mode == GRAM_SCORE ? launch_dm<64, GRAM_SCORE>(a, stream) : launch_dm<64, GRAM_REPAIR>(a, stream);
-  return mode == GRAM_SCORE ? launch_dm<128, GRAM_SCORE>(a, stream) : launch_dm<128, GRAM_REPAIR>(a, stream);
+  if (a.d == 64)
+    return mode == GRAM_SCORE ? launch_dm<Shape64, GRAM_SCORE>(a, stream) : launch_dm<Shape64Short, GRAM_REPAIR>(a, stream);
+  return mode == GRAM_SCORE ? launch_dm<Shape128, GRAM_SCORE>(a, stream) : launch_dm<Shape128, GRAM_REPAIR>(a, stream);
 }
 
 }  // namespace twinkv

@@ -85,7 +85,7 @@ def test_tiny_config_full():
     _run_score_select_repair(K, V, cfg, caps, do_repair_on_select=True, tag="cfg1")
 
 
-@pytest.mark.parametrize("cfg_id,G,N", [(2, 3, 1500), (2, 2, 513), (2, 1, 65), (4, 2, 1100), (3, 2, 700)])
+@pytest.mark.parametrize("cfg_id,G,N", [(2, 3, 1500), (2, 2, 513), (2, 1, 65), (4, 2, 1100), (3, 2, 700), (2, 1, 8300)])
 def test_score_select_ragged(cfg_id, G, N):
     cfg = get_config(cfg_id)
     K, V, _ = make_heads(cfg, heads=range(G), N=N)
