@@ -97,9 +97,15 @@ __device__ __forceinline__ void find_digit(SelectSmem& s, unsigned k) {
   }
 }
 
-// MSB-first radix select over positions [lo, hi) with pred(i) true:
-// returns T, the k-th largest key (1 <= k <= number of eligible positions);
-// *k_rem = k - #(key > T) is how many of the #(key == T) = *n_eq ties to take.
+// MSB-first radix select over positions [lo, hi) with pred(i) true, for the
+// k largest keys (1 <= k <= number of eligible positions).  Returns T such
+// that the selection is every key > T plus the first *k_rem keys == T (in
+// any order the caller fixes); *n_eq >= *k_rem.  Normally T is the k-th
+// largest key, *k_rem = k - #(key > T) and *n_eq = #(key == T).  The passes
+// stop early once every key sharing the digits found so far is selected:
+// then T is that prefix with the lower bits zero and *k_rem = *n_eq = the
+// number of keys sharing it, so all of them are either > T or == T and
+// taken, and no key outside the prefix lies between.
 template <class KeyOf, class Pred>
 __device__ uint64_t block_radix_select(int64_t lo, int64_t hi, unsigned k, KeyOf key_of, Pred pred, SelectSmem& s,
                                        unsigned* k_rem, unsigned* n_eq) {
@@ -122,6 +128,7 @@ __device__ uint64_t block_radix_select(int64_t lo, int64_t hi, unsigned k, KeyOf
     k -= s.above;
     neq = s.neq;
     __syncthreads();
+    if (neq == k) break;  // uniform: read from LDS after the barrier
   }
   *k_rem = k;
   *n_eq = neq;

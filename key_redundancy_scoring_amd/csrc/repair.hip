@@ -14,7 +14,7 @@
 //   Both rankings become "descending 64-bit key, ascending position": the key
 //   is the order-preserving bit image of b for donors and its complement for
 //   orphans.  On the side with more than m members a radix select finds the
-//   m-th key; the m chosen members of each side are gathered in position
+//   m-th key (or a prefix of it that only the chosen share); the m chosen members of each side are gathered in position
 //   order and put in rank order by a stable LSD radix sort, which keeps equal
 //   keys in position order.
 #include <limits.h>

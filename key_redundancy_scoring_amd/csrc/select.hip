@@ -6,10 +6,12 @@
 //
 // One 1024-thread workgroup per head.  Scores and energies are non-negative
 // fp64, so their bit patterns order like the values.  An MSB-first radix
-// select (8 passes of 8-bit digits) finds the u-th largest score; only if the
-// boundary value is shared by more positions than remain to be taken does a
-// second select run on the energies of those ties, and only if that boundary
-// is shared too are the remaining slots given to the lowest positions.  A
+// select (up to 8 passes of 8-bit digits; it stops as soon as the bucket of
+// the boundary digit is taken whole) finds the threshold of the u largest
+// scores; only if the boundary value is shared by more positions than remain
+// to be taken does a second select run on the energies of those ties, and
+// only if that boundary is shared too are the remaining slots given to the
+// lowest positions.  A
 // final pass in position order writes the keep mask and the ascending list of
 // retained positions.
 #include "blockops.h"
