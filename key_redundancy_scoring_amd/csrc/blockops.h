@@ -46,6 +46,37 @@ __device__ __forceinline__ int block_scan_flag(bool f, ScanSmem& s, int* total) 
   return off + pre;
 }
 
+struct ScanSmem2 {
+  int wave[2][kBW];
+};
+
+// Both exclusive prefixes of two 0/1 flags in one round of barriers.
+__device__ __forceinline__ void block_scan_flag2(bool f0, bool f1, ScanSmem2& s, int* pre0, int* pre1, int* tot0,
+                                                 int* tot1) {
+  const uint64_t m0 = __ballot(f0);
+  const uint64_t m1 = __ballot(f1);
+  if (lane_id() == 0) {
+    s.wave[0][wave_id()] = __popcll(m0);
+    s.wave[1][wave_id()] = __popcll(m1);
+  }
+  __syncthreads();
+  int o0 = 0, o1 = 0, t0 = 0, t1 = 0;
+#pragma unroll
+  for (int w = 0; w < kBW; ++w) {
+    const int v0 = s.wave[0][w];
+    const int v1 = s.wave[1][w];
+    o0 += (w < wave_id()) ? v0 : 0;
+    o1 += (w < wave_id()) ? v1 : 0;
+    t0 += v0;
+    t1 += v1;
+  }
+  __syncthreads();
+  *pre0 = o0 + __popcll(m0 & lanes_below());
+  *pre1 = o1 + __popcll(m1 & lanes_below());
+  *tot0 = t0;
+  *tot1 = t1;
+}
+
 __device__ __forceinline__ long long block_sum(long long v, long long* s_red) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);

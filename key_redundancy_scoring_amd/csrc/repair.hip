@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ k
 // Gather the top-m members of one side, in position order, into (lk, li).
 template <class KeyOf, class Pred>
 __device__ void collect_side(int64_t N, unsigned m, long long count, KeyOf key_of, Pred pred, uint64_t* lk,
-                             int32_t* li, SelectSmem& ss, ScanSmem& sc) {
+                             int32_t* li, SelectSmem& ss, ScanSmem2& sc) {
   const bool all = (long long)m == count;
   uint64_t T = 0;
   unsigned k_rem = 0, n_eq = 0;
@@ -126,24 +126,26 @@ __device__ void collect_side(int64_t N, unsigned m, long long count, KeyOf key_o
       if (all || key > T) take = true;
       else if (key == T) tie = true;
     }
-    int tt = 0;
-    const int tr = block_scan_flag(tie, sc, &tt);
-    if (tie && (unsigned)(tie_base + tr) < k_rem) take = true;
-    tie_base += tt;
-    int kt = 0;
-    const int kr = block_scan_flag(take, sc, &kt);
-    if (take) {
-      lk[base + kr] = key;
-      li[base + kr] = (int32_t)i;
+    // the ties taken are the first k_rem of all ties in position order, so
+    // in this chunk the first `rem` of its ties; a member's place among the
+    // chunk's chosen is the plain takes before it plus the taken ties before it
+    int tr = 0, kr = 0, tt = 0, kt = 0;
+    block_scan_flag2(tie, take, sc, &tr, &kr, &tt, &kt);
+    const int rem = (int)k_rem > tie_base ? (int)k_rem - tie_base : 0;
+    if (take || (tie && tr < rem)) {
+      const int r = kr + (tr < rem ? tr : rem);
+      lk[base + r] = key;
+      li[base + r] = (int32_t)i;
     }
-    base += kt;
+    base += kt + (tt < rem ? tt : rem);
+    tie_base += tt;
   }
   __syncthreads();
 }
 
 __global__ __launch_bounds__(kBT) void swap_kernel(SwapArgs a) {
   __shared__ SelectSmem ss;
-  __shared__ ScanSmem sc;
+  __shared__ ScanSmem2 sc;
   __shared__ SortSmem so;
   __shared__ long long red[kBW];
 

@@ -23,7 +23,7 @@ __device__ __forceinline__ uint64_t dbits(double x) { return (uint64_t)__double_
 
 __global__ __launch_bounds__(kBT) void select_kernel(SelectArgs a) {
   __shared__ SelectSmem ss;
-  __shared__ ScanSmem sc;
+  __shared__ ScanSmem2 sc;
   __shared__ long long red[kBW];
 
   const int64_t g = blockIdx.x;
@@ -98,18 +98,21 @@ __global__ __launch_bounds__(kBT) void select_kernel(SelectArgs a) {
         }
       }
     }
-    int tie_tot = 0;
-    const int trank = block_scan_flag(tie, sc, &tie_tot);
-    if (tie && (unsigned)(tie_base + trank) < k2) take = true;
-    tie_base += tie_tot;
-    int kept_tot = 0;
-    const int krank = block_scan_flag(take, sc, &kept_tot);
+    // the index-level ties kept are the first k2 of all such ties in
+    // position order, so in this chunk the first `rem` of its ties; a kept
+    // position's place is the other kept positions before it plus the kept
+    // ties before it
+    int trank = 0, krank = 0, tie_tot = 0, kept_tot = 0;
+    block_scan_flag2(tie, take, sc, &trank, &krank, &tie_tot, &kept_tot);
+    const int rem = (int)k2 > tie_base ? (int)k2 - tie_base : 0;
+    if (tie && trank < rem) take = true;
     if (in) a.keep[g * N + i] = take ? 1 : 0;
     if (take) {
-      const long long dst = off_g + kept_base + krank;
+      const long long dst = off_g + kept_base + krank + (trank < rem ? trank : rem);
       if (dst < a.kept_idx_len) a.kept_idx[dst] = (int32_t)i;
     }
-    kept_base += kept_tot;
+    kept_base += kept_tot + (tie_tot < rem ? tie_tot : rem);
+    tie_base += tie_tot;
   }
 }
 
