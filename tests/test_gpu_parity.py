@@ -223,6 +223,33 @@ def test_repair_noop_and_extremes():
     assert int(res["n_swaps"][0]) == 0 and int(res["n_swaps"][1]) == 0
 
 
+def test_repair_short_retained_sets():
+    """Retained sets shorter than a tile, a tile, a stage of the d = 64
+    restricted sweep (128 columns) and one more, at random positions, with and
+    without the score pass's twins as the prior, against the oracle."""
+    cfg = get_config(2)
+    sizes = [1, 3, 31, 32, 33, 127, 128, 129]
+    G, N = len(sizes), 700
+    K, V, _ = make_heads(cfg, heads=range(G), N=N)
+    rng = np.random.default_rng(20261203)
+    masks = np.zeros((G, N), np.uint8)
+    for g, k in enumerate(sizes):
+        masks[g, rng.choice(N, size=k, replace=False)] = 1
+    tk = _up(K)
+    prior = krs.score(tk, _up(V), cfg.tau, cfg.window, cfg.sink, cfg.recent)
+    keep_in = torch.from_numpy(masks).to(_dev())
+    plain = krs.repair(tk, keep_in, cfg.tau, cfg.window, cfg.sink, cfg.recent)
+    with_prior = krs.repair(tk, keep_in, cfg.tau, cfg.window, cfg.sink, cfg.recent, prior=prior)
+    torch.cuda.synchronize()
+    for g in range(G):
+        rref = PR.repair_reference(K[g], masks[g], cfg.tau, cfg.window, cfg.sink, cfg.recent)
+        for name, res in (("repair", plain), ("repair with prior", with_prior)):
+            rg = {k: res[k][g].cpu().numpy() for k in ("keep", "n_orphans", "n_donors", "n_swaps", "pairs")}
+            rg["best"] = res["best_sim"][g].cpu().numpy()
+            rg["arg"] = res["best_idx"][g].cpu().numpy()
+            PR.compare_repair(rg, rref, masks[g], cfg.tau, tag=f"short retained set K={sizes[g]} {name}")
+
+
 def test_deterministic_repeat():
     cfg = get_config(2)
     K, V, _ = make_heads(cfg, heads=range(4), N=2000)
