@@ -177,6 +177,7 @@ def main():
         cap_list = [int(c) for c in dirichlet_capacities(cfg)]
     caps = torch.tensor(cap_list, dtype=torch.int32, device=dev)
     offsets = krs.capacity_offsets(cap_list, N)
+    offsets_dev = krs.capacity_offsets_device(caps, N)
     s_out, sel_out, rep_out = {}, {}, {}
     s_ws = r_ws = None
 
@@ -186,7 +187,7 @@ def main():
         s_ws = r["ws"]
         s_out.update({k: r[k] for k in ("count", "best_sim", "best_idx", "energy", "score")})
         sl = krs.select(r["score"], r["energy"], caps, cfg.sink, cfg.recent, out=sel_out, events=ev_sel,
-                        offsets=offsets)
+                        offsets=offsets_dev)
         sel_out.update({"keep": sl["keep"], "kept_idx": sl["kept_idx"]})
         rp = krs.repair(K, sl["keep"], cfg.tau, cfg.window, cfg.sink, cfg.recent, prior=r, out=rep_out, ws=r_ws,
                         events=ev_r)
@@ -224,7 +225,6 @@ def main():
     # packed cache of the last step's selection (not part of the timed step)
     gev = [krs.Events(2) for _ in range(args.steps)]
     gout = {}
-    offsets_dev = torch.as_tensor(offsets, dtype=torch.int64).to(dev)
     for k in range(args.steps + 1):
         gres = krs.gather_kv(K, V, sel_out["kept_idx"], offsets_dev, total=int(offsets[-1]), out=gout,
                              events=gev[k - 1] if k else None)

@@ -84,7 +84,8 @@ typedef struct twinkv_params {
   int64_t N;      /* prefix length of every head, 1 <= N <= 2^30                             */
   int32_t d;      /* head dim: 64 or 128                                                    */
   int32_t window; /* local exclusion w >= 0: j is a twin candidate of i only if |i-j| > w
-                     ([P1] section 3.2; the pages' second page calls it l)                   */
+                     ([P1] section 3.2; the pages' second page calls it l); any w >= N - 1
+                     leaves no candidate                                                     */
   double tau;     /* similarity threshold, -1 < tau < 1 ([P1] Eq. 2 uses sim > tau)          */
   int32_t sink;   /* leading protected positions before clipping, >= 0 ([P2] section 3.1)   */
   int32_t recent; /* trailing protected positions before clipping, >= 0                     */
@@ -146,18 +147,31 @@ int twinkv_score(const twinkv_params* params, const void* keys, const void* valu
  * unprotected positions ranked first by (score desc, energy desc, position
  * asc) ([P2] 3.1, 3.2 tie rule, 3.4).
  *   keep[g][i]  (uint8 [G][N])  1 if retained, else 0
- *   kept_idx    (int32)         the retained positions of head g in ascending
- *                               order, at kept_idx[off_g .. off_g + b), where
- *                               off_g = sum over h < g of clamp(capacity[h]);
- *                               entries at or beyond kept_idx_len are not written
+ *   kept_idx    (int32 [kept_off[G]])  the retained positions of head g in
+ *               ascending (sequence) order at kept_idx[kept_off[g] ..
+ *               kept_off[g+1]) ([P2] 3.4: the kept indices stay in order)
  * score, energy: double [G][N] (as produced by twinkv_score; must be finite
- * and >= 0).  capacity: int32 [G].  Of the parameters only G, N, sink and
- * recent are read; workspace may be NULL (twinkv_workspace_bytes is 0).
+ * and >= 0).  capacity: int32 [G].  kept_off: int64 [G+1] device array of
+ * prefix sums of the clamped capacities (twinkv_capacity_offsets writes it).
+ * Writes to kept_idx stay inside [kept_off[g], min(kept_off[g+1],
+ * kept_off[G])), so offsets that do not match the capacities give wrong
+ * lists, never a write outside kept_idx's kept_off[G] entries.  Of the
+ * parameters only G, N, sink and recent are read; workspace may be NULL
+ * (twinkv_workspace_bytes is 0).
  * Phases for `marks`: 0 = select.
  */
 int twinkv_select(const twinkv_params* params, const double* score, const double* energy,
-                  const int32_t* capacity, uint8_t* keep, int32_t* kept_idx, int64_t kept_idx_len,
+                  const int32_t* capacity, const int64_t* kept_off, uint8_t* keep, int32_t* kept_idx,
                   void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* marks);
+
+/*
+ * twinkv_capacity_offsets - the kept_off array of twinkv_select and
+ * twinkv_gather_kv, on the device: kept_off[0] = 0 and kept_off[g+1] =
+ * kept_off[g] + clamp(capacity[g], 0, N) for g < G ([P2] 3.4: heads packed
+ * one after another).  capacity: int32 [G]; kept_off: int64 [G+1] (out).
+ * Requires 1 <= G < 2^31 and 1 <= N <= 2^30.  Asynchronous on `stream`.
+ */
+int twinkv_capacity_offsets(const int32_t* capacity, int64_t G, int64_t N, int64_t* kept_off, hipStream_t stream);
 
 /*
  * twinkv_repair - one-shot repair of the retained set S0 = {i : keep_in[g][i] != 0}
@@ -183,9 +197,10 @@ int twinkv_select(const twinkv_params* params, const double* score, const double
  *   those rows are copied and only the others are swept.  The outputs are the
  *   same as without a prior, except that such a row reports the prior's
  *   (exact fp64) choice where two positions' fp32 similarities are within
- *   rounding of each other.  An index outside [0, N) counts as not retained;
- *   any other inconsistent prior gives wrong results, never an access outside
- *   the stated sizes.  Both NULL: every row is swept.
+ *   rounding of each other.  An index outside [0, N) other than -1 counts as
+ *   not retained (that row is swept); any other inconsistent prior gives wrong
+ *   results, never an access outside the stated sizes.  Both NULL: every row
+ *   is swept.
  * Phases for `marks`: 0 = norms, 1 = compaction of S0 (retained positions and a
  * contiguous copy of their keys) and of the rows to sweep, 2 = restricted
  * Gram and fixup, 3 = classification, ranking and swap.

@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     Params,
     TwinKVError,
     capacity_offsets,
+    capacity_offsets_device,
     count_stats,
     gather_kv,
     header_symbols,

@@ -67,8 +67,10 @@ def load():
     lib.twinkv_status_string.restype = ctypes.c_char_p
     lib.twinkv_score.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.twinkv_score.restype = ctypes.c_int
-    lib.twinkv_select.argtypes = [P, vp, vp, vp, vp, vp, i64, vp, sz, vp, vp]
+    lib.twinkv_select.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.twinkv_select.restype = ctypes.c_int
+    lib.twinkv_capacity_offsets.argtypes = [vp, i64, i64, vp, vp]
+    lib.twinkv_capacity_offsets.restype = ctypes.c_int
     lib.twinkv_repair.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.twinkv_repair.restype = ctypes.c_int
     lib.twinkv_gather_kv.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp, vp]
@@ -240,20 +242,35 @@ def score(keys, values, tau, window, sink=4, recent=64, omega=False, out=None, w
 
 
 def capacity_offsets(capacity, N):
-    """Start of each head's run in ``kept_idx`` (host-side; clamped capacities)."""
+    """Start of each head's run in ``kept_idx`` for host capacities, on the
+    host (clamped capacities), to size buffers before a call."""
     c = torch.as_tensor(capacity).to("cpu", torch.int64).clamp(0, int(N))
     off = torch.zeros(c.numel() + 1, dtype=torch.int64)
     off[1:] = torch.cumsum(c, 0)
     return off
 
 
+def capacity_offsets_device(capacity, N, out=None):
+    """The same offsets computed by the library on the capacities' device
+    (twinkv_capacity_offsets), asynchronously on the current stream."""
+    lib = load()
+    if capacity.dtype != torch.int32 or not capacity.is_cuda or not capacity.is_contiguous():
+        raise ValueError("capacity must be a contiguous int32 device tensor")
+    G = capacity.numel()
+    off = _need(out, (G + 1,), torch.int64, capacity.device, "offsets")
+    _check(lib.twinkv_capacity_offsets(_ptr(capacity), G, int(N), _ptr(off), _stream()), "twinkv_capacity_offsets")
+    return off
+
+
 def select(score_t, energy_t, capacity, sink=4, recent=64, out=None, events=None, offsets=None):
-    """Exact-budget selection.  ``capacity``: int32 device tensor [G] (or a
-    host sequence, copied to the device).  ``offsets`` (optional): the host
-    offsets ``capacity_offsets(capacity, N)``; passing them avoids reading a
-    device capacity back to the host.  Returns keep (uint8 [G][N]), kept_idx
-    (int32, heads concatenated, ascending within a head) and the host-side
-    offsets of each head's run."""
+    """Exact-budget selection.  ``capacity``: int32 device tensor [G] or a
+    host sequence (copied to the device).  ``offsets`` (optional): int64
+    [G+1] prefix sums of the clamped capacities, on the host or the device.
+    Without them the library computes them on the device; the kept list is
+    then sized from the host capacities when they are on the host, else G*N
+    entries, so no device value is read back.  Returns keep (uint8 [G][N]),
+    kept_idx (int32, heads concatenated, ascending within a head), the device
+    offsets of each head's run and the device capacities."""
     lib = load()
     G, N = score_t.shape
     dev = score_t.device
@@ -266,23 +283,30 @@ def select(score_t, energy_t, capacity, sink=4, recent=64, out=None, events=None
         capacity = cap_host.to(dev)
     if capacity.dtype != torch.int32 or capacity.numel() != G or not capacity.is_contiguous():
         raise ValueError("capacity must be int32 [G]")
+    total = None
+    out = {} if out is None else out
     if offsets is not None:
         off = torch.as_tensor(offsets, dtype=torch.int64)
         if off.numel() != G + 1:
             raise ValueError("offsets must have G + 1 entries")
+        if off.device.type == "cpu":
+            total = int(off[-1])
+        off_dev = off if off.device == dev else off.to(dev)
     else:
-        off = capacity_offsets(cap_host if cap_host is not None else capacity.to("cpu"), N)
-    total = int(off[-1])
-    out = {} if out is None else out
+        off_dev = capacity_offsets_device(capacity, N, out=out.get("offsets"))
+        if cap_host is not None:
+            total = int(capacity_offsets(cap_host, N)[-1])
+    if total is None:
+        total = G * N
     keep = _need(out.get("keep"), (G, N), torch.uint8, dev, "keep")
     kept = out.get("kept_idx")
     if kept is None or kept.numel() < total:
         kept = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
     p = params(G, N, 0, 0.0, 0, sink, recent)  # select reads only G, N, sink, recent
-    st = lib.twinkv_select(ctypes.byref(p), _ptr(score_t), _ptr(energy_t), _ptr(capacity), _ptr(keep), _ptr(kept),
-                           total, ctypes.c_void_p(0), 0, _stream(), _marks(events, SELECT_PHASES))
+    st = lib.twinkv_select(ctypes.byref(p), _ptr(score_t), _ptr(energy_t), _ptr(capacity), _ptr(off_dev), _ptr(keep),
+                           _ptr(kept), ctypes.c_void_p(0), 0, _stream(), _marks(events, SELECT_PHASES))
     _check(st, "twinkv_select")
-    return {"keep": keep, "kept_idx": kept, "offsets": off, "capacity": capacity}
+    return {"keep": keep, "kept_idx": kept, "offsets": off_dev, "capacity": capacity}
 
 
 def repair(keys, keep_in, tau, window, sink=4, recent=64, prior=None, out=None, ws=None, events=None):

@@ -36,6 +36,11 @@ int check_params(const twinkv_params* p) {
   return TWINKV_OK;
 }
 
+// The window the kernels see.  A window of N or more leaves no nonlocal pair,
+// exactly as N itself does, and keeps the kernels' int32 band arithmetic
+// (position + window, position - window with positions below 2^30) in range.
+int32_t kernel_window(const twinkv_params* p) { return p->window < p->N ? p->window : (int32_t)p->N; }
+
 struct Carve {
   char* base;
   size_t off = 0;
@@ -211,7 +216,7 @@ int twinkv_score(const twinkv_params* p, const void* keys, const void* values, i
   ga.G = p->G;
   ga.N = p->N;
   ga.d = p->d;
-  ga.window = p->window;
+  ga.window = kernel_window(p);
   ga.tau = p->tau;
   ga.count = count;
   ga.best_sim = best_sim;
@@ -223,21 +228,27 @@ int twinkv_score(const twinkv_params* p, const void* keys, const void* values, i
   return TWINKV_OK;
 }
 
+int twinkv_capacity_offsets(const int32_t* capacity, int64_t G, int64_t N, int64_t* kept_off, hipStream_t stream) {
+  if (!capacity || !kept_off) return TWINKV_ERR_ARG;
+  if (G < 1 || G > (int64_t(1) << 31) - 1 || N < 1 || N > (int64_t(1) << 30)) return TWINKV_ERR_ARG;
+  TRY_HIP(launch_offsets(capacity, G, N, kept_off, stream));
+  return TWINKV_OK;
+}
+
 int twinkv_select(const twinkv_params* p, const double* score, const double* energy, const int32_t* capacity,
-                  uint8_t* keep, int32_t* kept_idx, int64_t kept_idx_len, void* workspace, size_t workspace_bytes,
+                  const int64_t* kept_off, uint8_t* keep, int32_t* kept_idx, void* workspace, size_t workspace_bytes,
                   hipStream_t stream, hipEvent_t* marks) {
   (void)workspace;
   (void)workspace_bytes;
   TRY(check_sizes(p));
-  if (!score || !energy || !capacity || !keep) return TWINKV_ERR_ARG;
-  if (kept_idx_len < 0 || (kept_idx_len > 0 && !kept_idx)) return TWINKV_ERR_ARG;
+  if (!score || !energy || !capacity || !kept_off || !keep || !kept_idx) return TWINKV_ERR_ARG;
   SelectArgs sa{};
   sa.score = score;
   sa.energy = energy;
   sa.capacity = capacity;
+  sa.kept_off = kept_off;
   sa.keep = keep;
   sa.kept_idx = kept_idx;
-  sa.kept_idx_len = kept_idx_len;
   sa.G = p->G;
   sa.N = p->N;
   sa.sink = p->sink;
@@ -385,7 +396,7 @@ int twinkv_repair(const twinkv_params* p, const void* keys, const uint8_t* keep_
   ga.G = p->G;
   ga.N = p->N;
   ga.d = p->d;
-  ga.window = p->window;
+  ga.window = kernel_window(p);
   ga.tau = p->tau;
   ga.best_sim = best_sim;
   ga.best_idx = best_idx;

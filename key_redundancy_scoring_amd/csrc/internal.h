@@ -42,13 +42,15 @@ struct SelectArgs {
   const double* score;
   const double* energy;
   const int32_t* capacity;
+  const int64_t* kept_off;  // [G+1] start of each head's run in kept_idx
   uint8_t* keep;
   int32_t* kept_idx;
-  int64_t kept_idx_len;
   int64_t G, N;
   int32_t sink, recent;
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+// kept_off[0] = 0, kept_off[g+1] = kept_off[g] + clamp(capacity[g], 0, N).
+hipError_t launch_offsets(const int32_t* capacity, int64_t G, int64_t N, int64_t* kept_off, hipStream_t stream);
 // Selection keys of a score variant (0 twin, 1 value, 2 rarity), optionally
 // with permuted counts.
 hipError_t launch_variant(const int32_t* count, const double* energy, const int32_t* perm, int64_t G, int64_t N,

@@ -50,7 +50,8 @@ __global__ __launch_bounds__(kBT) void compact_kernel(const uint8_t* __restrict_
 // position of S0 does.  If there is no nonlocal j at all (prior_idx = -1),
 // S0 has none either.  Those rows take the prior and are not swept; the
 // others are listed in ascending order.  Without a prior every row is
-// listed.  A prior index outside [0, N) is treated as not retained.
+// listed.  A prior index outside [0, N) other than -1 is treated as not
+// retained, so its row is swept.
 __global__ __launch_bounds__(kBT) void rows_kernel(const uint8_t* __restrict__ keep_in,
                                                    const double* __restrict__ prior_sim,
                                                    const int32_t* __restrict__ prior_idx, int64_t N,
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(kBT) void rows_kernel(const uint8_t* __restrict__ k
     bool f = i < N;
     if (f && prior_idx) {
       const int32_t j = prior_idx[o + i];
-      if (j < 0 || (j < N && keep_in[o + j] != 0)) {
+      if (j == -1 || (j >= 0 && j < N && keep_in[o + j] != 0)) {
         f = false;
         best_sim[o + i] = prior_sim[o + i];
         best_idx[o + i] = j;

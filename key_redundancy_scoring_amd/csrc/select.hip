@@ -24,7 +24,6 @@ __device__ __forceinline__ uint64_t dbits(double x) { return (uint64_t)__double_
 __global__ __launch_bounds__(kBT) void select_kernel(SelectArgs a) {
   __shared__ SelectSmem ss;
   __shared__ ScanSmem2 sc;
-  __shared__ long long red[kBW];
 
   const int64_t g = blockIdx.x;
   const int64_t N = a.N;
@@ -38,13 +37,13 @@ __global__ __launch_bounds__(kBT) void select_kernel(SelectArgs a) {
   const int64_t u = cap - s_cnt - r_cnt;
   const int64_t lo = s_cnt, hi = N - r_cnt;  // unprotected candidates [lo, hi)
 
-  // offset of this head's list: sum of clamped capacities of the heads before it
-  long long part = 0;
-  for (int64_t q = threadIdx.x; q < g; q += kBT) {
-    long long c = a.capacity[q];
-    part += c < 0 ? 0 : (c > N ? N : c);
-  }
-  const long long off_g = block_sum(part, red);
+  // this head's run of the kept list: [kept_off[g], kept_off[g+1]), clipped
+  // to the list's length kept_off[G], so inconsistent offsets can give wrong
+  // entries but never a write outside [0, kept_off[G])
+  const long long total = a.kept_off[a.G];
+  const long long off_g = a.kept_off[g];
+  long long off_end = a.kept_off[g + 1];
+  off_end = off_end < total ? off_end : total;
 
   // level 0: take no candidate; 1: all; 2: score > T1, ties resolved below
   int level;
@@ -109,10 +108,46 @@ __global__ __launch_bounds__(kBT) void select_kernel(SelectArgs a) {
     if (in) a.keep[g * N + i] = take ? 1 : 0;
     if (take) {
       const long long dst = off_g + kept_base + krank + (trank < rem ? trank : rem);
-      if (dst < a.kept_idx_len) a.kept_idx[dst] = (int32_t)i;
+      if (dst >= 0 && dst < off_end) a.kept_idx[dst] = (int32_t)i;
     }
     kept_base += kept_tot + (tie_tot < rem ? tie_tot : rem);
     tie_base += tie_tot;
+  }
+}
+
+// Start of each head's run in the kept list: kept_off[0] = 0 and
+// kept_off[g+1] = kept_off[g] + clamp(capacity[g], 0, N).  One workgroup scans
+// the heads in chunks of kBT: an inclusive scan inside each wave by shuffles,
+// then the wave totals through LDS.
+__global__ __launch_bounds__(kBT) void offsets_kernel(const int32_t* __restrict__ capacity, int64_t G, int64_t N,
+                                                      int64_t* __restrict__ kept_off) {
+  __shared__ long long wsum[kBW];
+  long long base = 0;
+  if (threadIdx.x == 0) kept_off[0] = 0;
+  for (int64_t c0 = 0; c0 < G; c0 += kBT) {
+    const int64_t q = c0 + threadIdx.x;
+    long long v = 0;
+    if (q < G) {
+      const long long c = capacity[q];
+      v = c < 0 ? 0 : (c > N ? N : c);
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long u = __shfl_up(v, off);
+      if (lane_id() >= off) v += u;
+    }
+    if (lane_id() == 63) wsum[wave_id()] = v;
+    __syncthreads();
+    long long before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kBW; ++w) {
+      const long long t = wsum[w];
+      before += (w < wave_id()) ? t : 0;
+      tot += t;
+    }
+    __syncthreads();
+    if (q < G) kept_off[q + 1] = base + before + v;
+    base += tot;
   }
 }
 
@@ -162,6 +197,11 @@ hipError_t launch_variant(const int32_t* count, const double* energy, const int3
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(variant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, count, energy, perm, G, N, variant,
                      score, tie);
+  return hipGetLastError();
+}
+
+hipError_t launch_offsets(const int32_t* capacity, int64_t G, int64_t N, int64_t* kept_off, hipStream_t stream) {
+  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kBT), 0, stream, capacity, G, N, kept_off);
   return hipGetLastError();
 }
 

@@ -16,7 +16,8 @@ FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: every call belo
 def test_library_exports_every_header_symbol():
     lib = krs.load()
     declared = krs.header_symbols()
-    assert declared == ["twinkv_allocate", "twinkv_allocate_workspace_bytes", "twinkv_count_stats",
+    assert declared == ["twinkv_allocate", "twinkv_allocate_workspace_bytes", "twinkv_capacity_offsets",
+                        "twinkv_count_stats",
                         "twinkv_gather_kv", "twinkv_repair",
                         "twinkv_score", "twinkv_select", "twinkv_status_string", "twinkv_uniform_capacity",
                         "twinkv_uniform_capacity_ceil", "twinkv_variant_score", "twinkv_workspace_bytes"]
@@ -83,13 +84,19 @@ def test_score_validation():
 def test_select_validation():
     lib = krs.load()
     p = krs.params(2, 100, 0, 0.0, 0)  # select ignores d, tau and window
-    call = lambda p, kept=FAKE, n=10, keep=FAKE: lib.twinkv_select(  # noqa: E731
-        ctypes.byref(p) if p is not None else None, FAKE, FAKE, FAKE, keep, kept, n, None, 0, None, None)
+    call = lambda p, kept=FAKE, off=FAKE, keep=FAKE: lib.twinkv_select(  # noqa: E731
+        ctypes.byref(p) if p is not None else None, FAKE, FAKE, FAKE, off, keep, kept, None, 0, None, None)
     assert call(None) == L.ERR_ARG
     assert call(krs.params(2, 0, 0, 0.0, 0)) == L.ERR_ARG
     assert call(p, keep=None) == L.ERR_ARG
-    assert call(p, kept=None, n=5) == L.ERR_ARG
-    assert call(p, n=-1) == L.ERR_ARG
+    assert call(p, kept=None) == L.ERR_ARG
+    assert call(p, off=None) == L.ERR_ARG
+    offs = lib.twinkv_capacity_offsets
+    assert offs(None, 2, 100, FAKE, None) == L.ERR_ARG
+    assert offs(FAKE, 2, 100, None, None) == L.ERR_ARG
+    assert offs(FAKE, 0, 100, FAKE, None) == L.ERR_ARG
+    assert offs(FAKE, 2, 0, FAKE, None) == L.ERR_ARG
+    assert offs(FAKE, 2, (1 << 30) + 1, FAKE, None) == L.ERR_ARG
 
 
 def test_repair_validation():

@@ -43,6 +43,51 @@ def test_figure3_normalised_scores():
     assert abs(e[0] * w2[0] - g["A"]["normalized_score"]) > tol
 
 
+def _bf16_exact(rows):
+    """bf16 bit patterns of values that bf16 holds exactly (asserted)."""
+    x = np.asarray(rows, dtype=np.float32)
+    u = x.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "value not exact in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def test_value_energy_closed_forms():
+    """e = ||v||^2 ([P2] section 3.2) on bf16-exact rows whose squared norm is
+    known in closed form: a 3-4-5 row gives 25 (||v|| would give 5), a row of
+    d halves gives d/4 (||v|| = sqrt(d)/2), a unit basis row 1, a zero row 0,
+    and a row mixing 2^10, 2^-10 and -2 the exact 2^20 + 4 + 2^-20 (which
+    fp64 holds; any dropped or doubled term changes it)."""
+    for d in (64, 128):
+        rows = np.zeros((5, d), np.float32)
+        rows[0, :2] = (3.0, 4.0)
+        rows[1, :] = 0.5
+        rows[2, d - 1] = 1.0
+        rows[4, [0, 7, d // 2]] = (2.0 ** 10, 2.0 ** -10, -2.0)
+        e = O.value_energy(O.widen_bf16(_bf16_exact(rows)))
+        assert e.tolist() == [25.0, d / 4.0, 1.0, 0.0, 2.0 ** 20 + 4.0 + 2.0 ** -20]
+
+
+def test_value_energy_reads_values_not_keys():
+    """Through the whole-head score: with keys and values that differ, the
+    energy and the score follow the values.  Keys are orthonormal basis rows
+    (no twins, count 0, score = e * ln(N+1)); values are 3-4 rows scaled by
+    the position, so e_i = 25 (i+1)^2 exactly."""
+    N, d = 16, 64
+    Kf = np.zeros((N, d), np.float32)
+    Kf[np.arange(N), np.arange(N)] = 1.0
+    Vf = np.zeros((N, d), np.float32)
+    Vf[:, 0] = 3.0 * (np.arange(N) + 1)
+    Vf[:, 1] = 4.0 * (np.arange(N) + 1)
+    r = O.score_head(_bf16_exact(Kf), _bf16_exact(Vf), 0.5, 2)
+    want = 25.0 * (np.arange(N) + 1.0) ** 2
+    assert r["energy"].tolist() == want.tolist()
+    assert np.all(r["count"] == 0)
+    np.testing.assert_allclose(r["score"], want * math.log(N + 1.0), rtol=1e-15, atol=0)
+    # the energy is not a function of the keys: swapping in other keys keeps it
+    r2 = O.score_head(_bf16_exact(Kf[::-1].copy()), _bf16_exact(Vf), 0.5, 2)
+    assert r2["energy"].tolist() == want.tolist()
+
+
 def test_discount_closed_forms():
     N = 1000
     c = np.arange(N)
