@@ -187,7 +187,7 @@ def main():
         s_ws = r["ws"]
         s_out.update({k: r[k] for k in ("count", "best_sim", "best_idx", "energy", "score")})
         sl = krs.select(r["score"], r["energy"], caps, cfg.sink, cfg.recent, out=sel_out, events=ev_sel,
-                        offsets=offsets_dev)
+                        offsets=offsets_dev, total=int(offsets[-1]))
         sel_out.update({"keep": sl["keep"], "kept_idx": sl["kept_idx"]})
         rp = krs.repair(K, sl["keep"], cfg.tau, cfg.window, cfg.sink, cfg.recent, prior=r, out=rep_out, ws=r_ws,
                         events=ev_r)

@@ -262,13 +262,15 @@ def capacity_offsets_device(capacity, N, out=None):
     return off
 
 
-def select(score_t, energy_t, capacity, sink=4, recent=64, out=None, events=None, offsets=None):
+def select(score_t, energy_t, capacity, sink=4, recent=64, out=None, events=None, offsets=None, total=None):
     """Exact-budget selection.  ``capacity``: int32 device tensor [G] or a
     host sequence (copied to the device).  ``offsets`` (optional): int64
     [G+1] prefix sums of the clamped capacities, on the host or the device.
     Without them the library computes them on the device; the kept list is
     then sized from the host capacities when they are on the host, else G*N
-    entries, so no device value is read back.  Returns keep (uint8 [G][N]),
+    entries, so no device value is read back; ``total`` (the sum of the
+    clamped capacities, when the caller knows it) sizes it exactly.  Returns
+    keep (uint8 [G][N]),
     kept_idx (int32, heads concatenated, ascending within a head), the device
     offsets of each head's run and the device capacities."""
     lib = load()
@@ -283,18 +285,17 @@ def select(score_t, energy_t, capacity, sink=4, recent=64, out=None, events=None
         capacity = cap_host.to(dev)
     if capacity.dtype != torch.int32 or capacity.numel() != G or not capacity.is_contiguous():
         raise ValueError("capacity must be int32 [G]")
-    total = None
     out = {} if out is None else out
     if offsets is not None:
         off = torch.as_tensor(offsets, dtype=torch.int64)
         if off.numel() != G + 1:
             raise ValueError("offsets must have G + 1 entries")
-        if off.device.type == "cpu":
+        if off.device.type == "cpu" and total is None:
             total = int(off[-1])
         off_dev = off if off.device == dev else off.to(dev)
     else:
         off_dev = capacity_offsets_device(capacity, N, out=out.get("offsets"))
-        if cap_host is not None:
+        if cap_host is not None and total is None:
             total = int(capacity_offsets(cap_host, N)[-1])
     if total is None:
         total = G * N

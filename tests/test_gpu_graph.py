@@ -33,11 +33,13 @@ def test_step_graph_replays_match_eager():
     tv = torch.from_numpy(V.view(np.int16)).to(dev)
     cap = O.uniform_budget(N, cfg.removal)
     caps = torch.full((G,), cap, dtype=torch.int32, device=dev)
-    off = krs.capacity_offsets([cap] * G, N)
+    off = krs.capacity_offsets_device(caps, N)
+    torch.cuda.synchronize()
+    assert torch.equal(off.cpu(), krs.capacity_offsets([cap] * G, N))
 
     # eager run: the reference, and the buffers the graph will write
     r = krs.score(tk, tv, cfg.tau, cfg.window, cfg.sink, cfg.recent)
-    sl = krs.select(r["score"], r["energy"], caps, cfg.sink, cfg.recent, offsets=off)
+    sl = krs.select(r["score"], r["energy"], caps, cfg.sink, cfg.recent, offsets=off, total=G * cap)
     rp = krs.repair(tk, sl["keep"], cfg.tau, cfg.window, cfg.sink, cfg.recent, prior=r)
     torch.cuda.synchronize()
     ref = {("s", k): r[k].clone() for k in SCORE_KEYS}
@@ -53,7 +55,8 @@ def test_step_graph_replays_match_eager():
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph, stream=side):
             r2 = krs.score(tk, tv, cfg.tau, cfg.window, cfg.sink, cfg.recent, out=s_out, ws=r["ws"])
-            sl2 = krs.select(r2["score"], r2["energy"], caps, cfg.sink, cfg.recent, out=sel_out, offsets=off)
+            sl2 = krs.select(r2["score"], r2["energy"], caps, cfg.sink, cfg.recent, out=sel_out, offsets=off,
+                             total=G * cap)
             krs.repair(tk, sl2["keep"], cfg.tau, cfg.window, cfg.sink, cfg.recent, prior=r2, out=rep_out,
                        ws=rp["ws"])
     torch.cuda.current_stream().wait_stream(side)

@@ -208,6 +208,19 @@ def test_capacity_edges_and_clamping():
         np.testing.assert_array_equal(sel["kept_idx"].cpu().numpy()[off[g]:off[g + 1]], oi)
 
 
+def test_capacity_offsets_device_clamps_and_spans_chunks():
+    """twinkv_capacity_offsets against the host prefix sums of the clamped
+    capacities, over more heads than one workgroup's chunk of 1024."""
+    rng = np.random.default_rng(5)
+    N = 777
+    for G in (1, 1024, 2500):
+        caps = rng.integers(-5, N + 6, size=G).astype(np.int32)
+        got = krs.capacity_offsets_device(torch.from_numpy(caps).to(_dev()), N)
+        torch.cuda.synchronize()
+        want = np.concatenate([[0], np.cumsum(np.clip(caps.astype(np.int64), 0, N))])
+        np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=f"G={G}")
+
+
 def test_repair_noop_and_extremes():
     cfg = get_config(3)
     G, N = 4, 600
