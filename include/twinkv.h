@@ -56,7 +56,8 @@
  *     immediately before launching phase k and marks[P] after the last
  *     launch, where P is the phase count documented per entry point.  It
  *     serves only to time the phases.
- *   - No exception crosses the ABI; there is no global state.
+ *   - No exception crosses the ABI.  The only global state is the
+ *     per-device static scratch of twinkv_score_noalloc.
  */
 #ifndef TWINKV_H
 #define TWINKV_H
@@ -75,7 +76,8 @@ typedef enum twinkv_status {
   TWINKV_ERR_ARG = -1,         /* a null pointer, a size out of range, a bad parameter */
   TWINKV_ERR_UNSUPPORTED = -2, /* head dim other than 64 or 128                        */
   TWINKV_ERR_WORKSPACE = -3,   /* workspace smaller than twinkv_workspace_bytes()       */
-  TWINKV_ERR_HIP = -4          /* the HIP runtime refused a launch or an event record   */
+  TWINKV_ERR_HIP = -4,         /* the HIP runtime refused a launch or an event record   */
+  TWINKV_ERR_TOO_LARGE = -5    /* G*N beyond the static scratch of twinkv_score_noalloc */
 } twinkv_status;
 
 /* Problem description shared by all entry points. */
@@ -139,6 +141,31 @@ int twinkv_score(const twinkv_params* params, const void* keys, const void* valu
                  int32_t* count, double* best_sim, int32_t* best_idx, double* energy,
                  double* score, double* omega, void* workspace, size_t workspace_bytes,
                  hipStream_t stream, hipEvent_t* marks);
+
+/*
+ * twinkv_score_noalloc - twinkv_score for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and the same outputs,
+ * bit for bit, with the norms pass's scratch (fp64 squared norms and fp32
+ * inverse norms, 12 bytes per key) taken from a static device array of the
+ * library instead of a workspace argument.  Neither this call nor the
+ * library allocates or frees anything; the array, sized for
+ * TWINKV_NOALLOC_MAX_KEYS keys (24 MiB), is part of the library's device
+ * code and each device it runs on holds its own copy until the process
+ * ends.  The scratch used is the current device's (hipGetDevice), so
+ * `stream` must belong to it; its address is looked up on the first call on
+ * each device.  Every call on a device shares that device's scratch and it
+ * keeps the last call's contents (each call writes every entry it reads
+ * before reading it): calls that overlap on one device, on different
+ * streams or from different threads, race and give wrong results.
+ * Arguments and outputs as twinkv_score; G*N > TWINKV_NOALLOC_MAX_KEYS
+ * returns TWINKV_ERR_TOO_LARGE before anything is launched.
+ * Phases for `marks`: as twinkv_score.
+ */
+enum { TWINKV_NOALLOC_MAX_KEYS = 1 << 21 };
+int twinkv_score_noalloc(const twinkv_params* params, const void* keys, const void* values, int32_t* count,
+                         double* best_sim, int32_t* best_idx, double* energy, double* score, double* omega,
+                         hipStream_t stream, hipEvent_t* marks);
 
 /*
  * twinkv_select - per head g with capacity b = capacity[g] (0 <= b <= N;

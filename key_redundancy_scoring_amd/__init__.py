@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     params,
     repair,
     score,
+    score_noalloc,
     select,
     status_string,
     uniform_capacity,

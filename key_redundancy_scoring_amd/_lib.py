@@ -19,7 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtwinkv.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "twinkv.h")
 
-OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5
+NOALLOC_MAX_KEYS = 1 << 21
 OP_SCORE, OP_SELECT, OP_REPAIR = 0, 1, 2
 SCORE_PHASES, SELECT_PHASES, REPAIR_PHASES, GATHER_PHASES, ALLOC_PHASES, VARIANT_PHASES = 2, 1, 4, 1, 3, 1
 VARIANTS = {"twin": 0, "value": 1, "rarity": 2}
@@ -67,6 +68,8 @@ def load():
     lib.twinkv_status_string.restype = ctypes.c_char_p
     lib.twinkv_score.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.twinkv_score.restype = ctypes.c_int
+    lib.twinkv_score_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.twinkv_score_noalloc.restype = ctypes.c_int
     lib.twinkv_select.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.twinkv_select.restype = ctypes.c_int
     lib.twinkv_capacity_offsets.argtypes = [vp, i64, i64, vp, vp]
@@ -238,6 +241,37 @@ def score(keys, values, tau, window, sink=4, recent=64, omega=False, out=None, w
                           _stream(), _marks(events, SCORE_PHASES))
     _check(st, "twinkv_score")
     o["ws"] = ws
+    return o
+
+
+def score_noalloc(keys, values, tau, window, sink=4, recent=64, omega=False, out=None, events=None):
+    """score() through twinkv_score_noalloc: the library's static per-device
+    scratch instead of a workspace (G*N at most NOALLOC_MAX_KEYS).  Output
+    tensors are allocated here unless given in ``out``; the library call
+    itself allocates nothing.  Calls that overlap on one device race."""
+    lib = load()
+    keys = _as_bf16_bits(keys, "keys")
+    values = _as_bf16_bits(values, "values")
+    if values.shape != keys.shape:
+        raise ValueError("keys and values must have the same shape")
+    G, N, d = keys.shape
+    dev = keys.device
+    p = params(G, N, d, tau, window, sink, recent)
+    out = {} if out is None else out
+    o = {
+        "count": _need(out.get("count"), (G, N), torch.int32, dev, "count"),
+        "best_sim": _need(out.get("best_sim"), (G, N), torch.float64, dev, "best_sim"),
+        "best_idx": _need(out.get("best_idx"), (G, N), torch.int32, dev, "best_idx"),
+        "energy": _need(out.get("energy"), (G, N), torch.float64, dev, "energy"),
+        "score": _need(out.get("score"), (G, N), torch.float64, dev, "score"),
+    }
+    if omega or out.get("omega") is not None:
+        o["omega"] = _need(out.get("omega"), (G, N), torch.float64, dev, "omega")
+    with torch.cuda.device(dev):
+        st = lib.twinkv_score_noalloc(ctypes.byref(p), _ptr(keys), _ptr(values), _ptr(o["count"]),
+                                      _ptr(o["best_sim"]), _ptr(o["best_idx"]), _ptr(o["energy"]), _ptr(o["score"]),
+                                      _ptr(o.get("omega")), _stream(), _marks(events, SCORE_PHASES))
+    _check(st, "twinkv_score_noalloc")
     return o
 
 

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "twinkv.h"
 #include "internal.h"
 
@@ -13,7 +15,7 @@ using namespace twinkv;
 
 constexpr size_t kAlign = 256;
 
-size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+constexpr size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -118,6 +120,75 @@ int record(hipEvent_t* marks, int k, hipStream_t s) {
     if (_rc != TWINKV_OK) return _rc; \
   } while (0)
 
+int check_score_args(const twinkv_params* p, const void* keys, const void* values, const int32_t* count,
+                     const double* best_sim, const int32_t* best_idx, const double* energy, const double* score) {
+  TRY(check_params(p));
+  if (!keys || !values || !count || !best_sim || !best_idx || !energy || !score) return TWINKV_ERR_ARG;
+  if (!aligned16(keys) || !aligned16(values)) return TWINKV_ERR_ARG;
+  return TWINKV_OK;
+}
+
+// Norms pass, then the fused Gram sweep, over caller-checked arguments with
+// the squared norms and inverse norms at nsq and rinv.
+int score_launch(const twinkv_params* p, const void* keys, const void* values, int32_t* count, double* best_sim,
+                 int32_t* best_idx, double* energy, double* score, double* omega, double* nsq, float* rinv,
+                 hipStream_t stream, hipEvent_t* marks) {
+  const size_t n = (size_t)p->G * (size_t)p->N;
+  TRY(record(marks, 0, stream));
+  TRY_HIP(launch_norms(static_cast<const uint16_t*>(keys), static_cast<const uint16_t*>(values), (int64_t)n, p->d,
+                       nsq, rinv, energy, stream));
+  TRY(record(marks, 1, stream));
+  GramArgs ga{};
+  ga.keys = static_cast<const uint16_t*>(keys);
+  ga.nsq = nsq;
+  ga.col_keys = ga.keys;
+  ga.col_rinv = rinv;
+  ga.energy = energy;
+  ga.G = p->G;
+  ga.N = p->N;
+  ga.d = p->d;
+  ga.window = kernel_window(p);
+  ga.tau = p->tau;
+  ga.count = count;
+  ga.best_sim = best_sim;
+  ga.best_idx = best_idx;
+  ga.score = score;
+  ga.omega = omega;
+  TRY_HIP(launch_gram(ga, GRAM_SCORE, stream));
+  TRY(record(marks, 2, stream));
+  return TWINKV_OK;
+}
+
+// Scratch of twinkv_score_noalloc: the squared norms (fp64) and inverse
+// norms (fp32) of up to TWINKV_NOALLOC_MAX_KEYS keys, carved like a score
+// workspace.  Each device the library runs on holds its own copy for the
+// life of the process.  In host code `scratch` names a host-side stand-in,
+// never the device memory: its device address is looked up once per device
+// with hipGetSymbolAddress and only that address is handed to kernels.
+constexpr size_t kScratchBytes =
+    align_up((size_t)TWINKV_NOALLOC_MAX_KEYS * sizeof(double)) + align_up((size_t)TWINKV_NOALLOC_MAX_KEYS * sizeof(float));
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_addr[kMaxDevices];  // device address of `scratch`, per device; null until looked up
+
+// Device address of the current device's scratch, looked up on the first
+// call on that device (with it current) and kept.
+int scratch_of_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return TWINKV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return TWINKV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr) return TWINKV_ERR_HIP;
+    g_scratch_addr[dev] = static_cast<char*>(addr);
+  }
+  *out = g_scratch_addr[dev];
+  return TWINKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,6 +200,7 @@ const char* twinkv_status_string(int status) {
     case TWINKV_ERR_UNSUPPORTED: return "unsupported head dimension (64 or 128 only)";
     case TWINKV_ERR_WORKSPACE: return "workspace too small";
     case TWINKV_ERR_HIP: return "HIP runtime error";
+    case TWINKV_ERR_TOO_LARGE: return "problem larger than the static scratch (G*N > TWINKV_NOALLOC_MAX_KEYS)";
     default: return "unknown status";
   }
 }
@@ -191,41 +263,31 @@ size_t twinkv_workspace_bytes(int op, const twinkv_params* p) {
 int twinkv_score(const twinkv_params* p, const void* keys, const void* values, int32_t* count, double* best_sim,
                  int32_t* best_idx, double* energy, double* score, double* omega, void* workspace,
                  size_t workspace_bytes, hipStream_t stream, hipEvent_t* marks) {
-  TRY(check_params(p));
-  if (!keys || !values || !count || !best_sim || !best_idx || !energy || !score) return TWINKV_ERR_ARG;
-  if (!aligned16(keys) || !aligned16(values)) return TWINKV_ERR_ARG;
+  TRY(check_score_args(p, keys, values, count, best_sim, best_idx, energy, score));
   const size_t need = score_ws(p);
   if (!workspace || workspace_bytes < need) return TWINKV_ERR_WORKSPACE;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return TWINKV_ERR_ARG;
-
   Carve cv{static_cast<char*>(workspace)};
   const size_t n = (size_t)p->G * (size_t)p->N;
   double* nsq = cv.take<double>(n);
   float* rinv = cv.take<float>(n);
+  return score_launch(p, keys, values, count, best_sim, best_idx, energy, score, omega, nsq, rinv, stream, marks);
+}
 
-  TRY(record(marks, 0, stream));
-  TRY_HIP(launch_norms(static_cast<const uint16_t*>(keys), static_cast<const uint16_t*>(values), (int64_t)n, p->d,
-                       nsq, rinv, energy, stream));
-  TRY(record(marks, 1, stream));
-  GramArgs ga{};
-  ga.keys = static_cast<const uint16_t*>(keys);
-  ga.nsq = nsq;
-  ga.col_keys = ga.keys;
-  ga.col_rinv = rinv;
-  ga.energy = energy;
-  ga.G = p->G;
-  ga.N = p->N;
-  ga.d = p->d;
-  ga.window = kernel_window(p);
-  ga.tau = p->tau;
-  ga.count = count;
-  ga.best_sim = best_sim;
-  ga.best_idx = best_idx;
-  ga.score = score;
-  ga.omega = omega;
-  TRY_HIP(launch_gram(ga, GRAM_SCORE, stream));
-  TRY(record(marks, 2, stream));
-  return TWINKV_OK;
+int twinkv_score_noalloc(const twinkv_params* p, const void* keys, const void* values, int32_t* count,
+                         double* best_sim, int32_t* best_idx, double* energy, double* score, double* omega,
+                         hipStream_t stream, hipEvent_t* marks) {
+  TRY(check_score_args(p, keys, values, count, best_sim, best_idx, energy, score));
+  if (p->G * p->N > TWINKV_NOALLOC_MAX_KEYS) return TWINKV_ERR_TOO_LARGE;
+  char* base = nullptr;
+  TRY(scratch_of_current_device(&base));
+  // the same carving as a workspace: nsq, then rinv, each 256-byte aligned;
+  // the norms pass writes every entry the sweep reads, so nothing is cleared
+  Carve cv{base};
+  const size_t n = (size_t)p->G * (size_t)p->N;
+  double* nsq = cv.take<double>(n);
+  float* rinv = cv.take<float>(n);
+  return score_launch(p, keys, values, count, best_sim, best_idx, energy, score, omega, nsq, rinv, stream, marks);
 }
 
 int twinkv_capacity_offsets(const int32_t* capacity, int64_t G, int64_t N, int64_t* kept_off, hipStream_t stream) {

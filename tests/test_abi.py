@@ -19,7 +19,7 @@ def test_library_exports_every_header_symbol():
     assert declared == ["twinkv_allocate", "twinkv_allocate_workspace_bytes", "twinkv_capacity_offsets",
                         "twinkv_count_stats",
                         "twinkv_gather_kv", "twinkv_repair",
-                        "twinkv_score", "twinkv_select", "twinkv_status_string", "twinkv_uniform_capacity",
+                        "twinkv_score", "twinkv_score_noalloc", "twinkv_select", "twinkv_status_string", "twinkv_uniform_capacity",
                         "twinkv_uniform_capacity_ceil", "twinkv_variant_score", "twinkv_workspace_bytes"]
     for name in declared:
         assert hasattr(lib, name), name
