@@ -1,32 +1,43 @@
 """Benchmark of the key-redundancy hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+                    [--results-dir DIR]
     python bench.py --calibrate-copy        # plain device copy, for counter calibration
 
-One step = one pass of the whole path over one batch of synthetic heads that
-is already resident in HBM: score (norms/energy pass + fused Gram sweep with
-the fp64 best-twin fixup and the discounted score) -> exact-budget select ->
-repair of the selected set (compaction of the retained keys, restricted Gram
-over them, orphan/donor ranking and swap).  The default workload is the
-Llama-3.2-1B shape: 16 layers x 8 KV heads = 128 heads, N = 32768, head dim
-64, 10% planted near-duplicates, tau 0.9, window 64, 4 sinks, 64 recent, 50%
-removal.
+One step = one pass of the workload's whole path over one batch of synthetic
+heads that is already resident in HBM:
 
-Prints one JSON line.  `value` is keys (head positions) through the whole path
-per second.  `gather_kv` times, outside the step, the packed cache of the
-last step's selection (retained keys and values in sequence order),
-`variant_score` the keys of the permuted-count variant, `count_stats` the
-per-head count statistics against value-only selection, and `allocate` the per-head capacities from the attention of the last 32
-synthetic prefix queries of each KV head (8 KV heads per layer).  `roofline` is for the dominant kernel, the score-mode Gram
-sweep, timed with HIP events that the library records around its launch on
-the stream it runs on; its `achieved` counts the algorithmic work, one
-d-length dot product (2d flop) per unordered nonlocal pair, while `gram`
-also gives the dense-equivalent rate (both orders of every pair, the work the
-sweep executes).  `traffic` is the HBM traffic per launch measured with
-rocprofv3 counters for the current Gram source (null when the source has
-changed since).  `cpu_baseline` times the fp64 oracle's whole step (score,
-select, repair of the selection) on whole heads of the same workload, on the
-host, for about `--cpu-seconds` (at least one head).
+* score workloads (tiny, Llama-3.2-1B 32k -- the default --, long 131k,
+  batched 8k): score (norms/energy pass + fused Gram sweep with the fp64
+  best-twin fixup and the discounted score) -> exact-budget select -> repair
+  of the selected set (compaction of the retained keys, restricted Gram over
+  them for the rows whose unrestricted twin was evicted, orphan/donor
+  ranking and swap);
+* the Qwen3-4B repair workload (--config 3): repair of a given retained set,
+  the top half of each head by an i.i.d. Gumbel score, with no score pass
+  and no prior: every row is swept against the K = N/2 retained columns.
+
+Prints one JSON line.  `value` is keys (head positions) through the whole
+path per second.  `roofline` is for the dominant kernel (the score-mode Gram
+sweep; the restricted repair sweep in the repair workload), timed with HIP
+events that the library records around its launch on the stream it runs on.
+Its `achieved` counts the algorithmic work: one d-length dot product (2d
+flop) per unordered nonlocal pair in score mode, per (row, retained column)
+pair in repair mode; `gram` also gives the dense-equivalent rate (both orders
+of every pair, the work the score sweep executes).  `traffic` is the HBM
+traffic per launch measured with rocprofv3 counters for the current Gram
+source (null when the source has changed since).  Outside the timed step,
+`gather_kv` times the packed cache of the last step's retained set, and in
+score workloads `variant_score` the keys of the permuted-count variant,
+`count_stats` the per-head count statistics against value-only selection and
+`allocate` the per-head capacities from the attention of the last 32
+synthetic prefix queries of each KV head (8 KV heads per layer).
+
+`cpu_baseline` runs before the GPU is touched: the fp64 oracle's whole step
+on whole heads (one seeded head per host core, first and last head
+included), one head per process with one BLAS thread each, on
+min(16, len(os.sched_getaffinity(0))) processes; its value is the keys of
+those heads over the pool's wall time.
 """
 from __future__ import annotations
 
@@ -50,6 +61,7 @@ PEAK_FP64_TFLOPS = 78.6
 GRAM_SOURCE = os.path.join(ROOT, "key_redundancy_scoring_amd", "csrc", "gram.hip")
 # launch shape of the score-mode sweep per head dim, as the kernel trace names it
 SCORE_SHAPE = {64: "GramShape<64, 4, 4, 256, 2>", 128: "GramShape<128, 2, 4, 128, 2>"}
+REPAIR_SHAPE = {64: "GramShape<64, 2, 4, 128, 3>", 128: "GramShape<128, 2, 4, 128, 2>"}
 
 # HBM traffic of one score-mode Gram launch on the default workload, from
 # rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the counters'
@@ -58,6 +70,7 @@ SCORE_SHAPE = {64: "GramShape<64, 4, 4, 256, 2>", 128: "GramShape<128, 2, 4, 128
 MEASURED_TRAFFIC: dict = {
     "8e228c205b2f4f0945eb331799a250fe6168612366bc8425fb4467f59077fa47": {
         "workload": (128, 32768, 64),
+        "kernel": "gram_kernel<GramShape<64, 4, 4, 256, 2>, score>",
         # FETCH_SIZE 1875232.2 KiB x 1.99994 (a 1 GiB copy reads 524302.6 KiB),
         # WRITE_SIZE 114688.0 KiB x 1.0 (the same copy writes 1048576 KiB)
         "fetch_bytes": 3840368895,
@@ -83,32 +96,60 @@ def restricted_gram_flops(N: int, K: int, d: int, G: int) -> float:
     return float(G) * N * K * 2.0 * d
 
 
-def cpu_baseline(cfg, seconds: float, capacities):
-    """The oracle's whole step (score, select and repair of the selection:
-    count, best nonlocal twin, energy and score of every row against all N
-    positions, the exact-budget selection, then the best surviving twin of
-    every row against the retained set and the swap) on whole heads 0, 1, ...
-    until about `seconds` of host time are spent (at least one head); timed
-    on the host.  The same work per key as the GPU step."""
-    from threadpoolctl import threadpool_info
+def _oracle_step(job):
+    """The oracle's whole step on one head (runs in a pool worker)."""
+    cfg_id, overrides, g, capacity = job
+    from threadpoolctl import threadpool_limits
 
     from oracle import twinkv_oracle as O
-    from synth import make_head
+    from synth import get_config, gumbel_retained, make_head
 
-    done, spent, g = 0, 0.0, 0
-    while (spent < seconds or g == 0) and g < cfg.G:
-        h = make_head(cfg, g)
+    cfg = get_config(cfg_id, **overrides)
+    h = make_head(cfg, g)
+    with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        ref = O.score_head(h["K"], h["V"], cfg.tau, cfg.window)
-        keep, _ = O.select_head(ref["score"], ref["energy"], int(capacities[g]), cfg.sink, cfg.recent)
-        O.repair_head(O.widen_bf16(h["K"]), keep, cfg.tau, cfg.window, cfg.sink, cfg.recent)
-        spent += time.perf_counter() - t0
-        done += cfg.N
-        g += 1
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": done / spent, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"the whole step (score, select, repair of the selection) of head{'s 0..' if g > 1 else ' '}"
-                      f"{g - 1} at N={cfg.N}, fp64 numpy/BLAS, {spent:.1f} s"}
+        if cfg.mode == "repair":
+            O.repair_head(O.widen_bf16(h["K"]), gumbel_retained(cfg, g), cfg.tau, cfg.window, cfg.sink, cfg.recent)
+        else:
+            ref = O.score_head(h["K"], h["V"], cfg.tau, cfg.window)
+            keep, _ = O.select_head(ref["score"], ref["energy"], int(capacity), cfg.sink, cfg.recent)
+            O.repair_head(O.widen_bf16(h["K"]), keep, cfg.tau, cfg.window, cfg.sink, cfg.recent)
+        return time.perf_counter() - t0
+
+
+def baseline_heads(G: int, count: int, cfg_id: int) -> list:
+    """A seeded sample of `count` heads that includes the first and the last."""
+    if count >= G:
+        return list(range(G))
+    rng = np.random.default_rng([cfg_id, 4242])
+    mid = rng.choice(np.arange(1, G - 1), size=max(0, count - 2), replace=False)
+    return sorted({0, G - 1, *[int(x) for x in mid]})
+
+
+def cpu_baseline(cfg, overrides: dict, capacities, cores: int | None = None):
+    """The fp64 oracle's whole step (as the GPU step: score, select and repair
+    of the selection; repair of the Gumbel set in the repair workload) on
+    whole heads, one head per host core in a process pool, one BLAS thread
+    per process.  Must run before the GPU is initialised (the pool forks)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    affinity = len(os.sched_getaffinity(0))
+    cores = min(16, affinity) if cores is None else cores
+    heads = baseline_heads(cfg.G, cores, cfg.cfg_id)
+    jobs = [(cfg.cfg_id, overrides, g, capacities[g] if capacities is not None else 0) for g in heads]
+    t0 = time.perf_counter()
+    with cf.ProcessPoolExecutor(max_workers=len(jobs), mp_context=mp.get_context("fork")) as ex:
+        per_head = list(ex.map(_oracle_step, jobs))
+    wall = time.perf_counter() - t0
+    what = "repair of the Gumbel retained set" if cfg.mode == "repair" else \
+        "score, select, repair of the selection"
+    return {"value": len(heads) * cfg.N / wall, "unit": "keys/s", "cores": len(jobs), "kind": "oracle",
+            "sample": f"the oracle's whole step ({what}) of {len(heads)} whole heads at N={cfg.N} "
+                      f"(heads {heads[0]}..{heads[-1]}, seeded), one head per process, one BLAS thread each, "
+                      f"fp64 numpy; pool wall {wall:.1f} s, per head {min(per_head):.1f}-{max(per_head):.1f} s; "
+                      f"{affinity} cores in the affinity mask",
+            "heads": heads, "wall_s": wall}
 
 
 def calibrate_copy():
@@ -125,6 +166,37 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_per_launch": n}), flush=True)
 
 
+def _upload_heads(cfg, torch, dev):
+    G, N, d = cfg.G, cfg.N, cfg.d
+    from synth import make_heads
+
+    K = torch.empty((G, N, d), dtype=torch.int16, device=dev)
+    V = torch.empty((G, N, d), dtype=torch.int16, device=dev) if cfg.mode != "repair" else None
+    chunk = 32
+    for h0 in range(0, G, chunk):
+        hs = list(range(h0, min(G, h0 + chunk)))
+        k, v, _ = make_heads(cfg, heads=hs, with_values=V is not None)
+        K[h0:h0 + len(hs)].copy_(torch.from_numpy(k.view(np.int16)))
+        if V is not None:
+            V[h0:h0 + len(hs)].copy_(torch.from_numpy(v.view(np.int16)))
+    return K, V
+
+
+def _timed(fn, steps, nev, krs):
+    """Run fn(events) `steps` times after one untimed call; average the phase
+    times the events bracket."""
+    evs = [krs.Events(nev) for _ in range(steps)]
+    out = None
+    for k in range(steps + 1):
+        out = fn(evs[k - 1] if k else None)
+    import torch
+    torch.cuda.synchronize()
+    ms = [float(np.mean([e.elapsed_ms(a, a + 1) for e in evs])) for a in range(nev - 1)]
+    for e in evs:
+        e.close()
+    return out, ms
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,8 +204,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--heads", type=int, default=None, help="override the head count (default: the workload's)")
+    ap.add_argument("--results-dir", default=None, help="also write the line to DIR/<workload>.bench.json")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
 
@@ -145,52 +217,62 @@ def main():
         calibrate_copy()
         return
 
+    from synth import dirichlet_capacities, get_config, gumbel_retained
+
+    overrides = {"G": args.heads} if args.heads else {}
+    cfg = get_config(args.config, **overrides)
+    G, N, d = cfg.G, cfg.N, cfg.d
+    repair_mode = cfg.mode == "repair"
+    if repair_mode:
+        cap_list = None
+    elif cfg.removal is not None:
+        cap_list = [int(np.floor(N * (1.0 - cfg.removal)))] * G
+    else:
+        cap_list = [int(c) for c in dirichlet_capacities(cfg)]
+
+    # the oracle on the host cores first, before anything initialises the GPU
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, overrides, cap_list)
+        print(f"# cpu baseline: {cpu['sample']}", file=sys.stderr, flush=True)
+
     import torch
 
     import key_redundancy_scoring_amd as krs
-    from synth import dirichlet_capacities, get_config, make_heads
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a ROCm GPU")
     dev = torch.device("cuda:0")
-    cfg = get_config(args.config)
-    if args.heads:
-        cfg = cfg.with_(G=args.heads)
-    G, N, d = cfg.G, cfg.N, cfg.d
 
     t0 = time.perf_counter()
-    K = torch.empty((G, N, d), dtype=torch.int16, device=dev)
-    V = torch.empty((G, N, d), dtype=torch.int16, device=dev)
-    chunk = 32
-    for h0 in range(0, G, chunk):
-        hs = list(range(h0, min(G, h0 + chunk)))
-        k, v, _ = make_heads(cfg, heads=hs)
-        K[h0:h0 + len(hs)].copy_(torch.from_numpy(k.view(np.int16)))
-        V[h0:h0 + len(hs)].copy_(torch.from_numpy(v.view(np.int16)))
+    K, V = _upload_heads(cfg, torch, dev)
+    S0 = None
+    if repair_mode:
+        S0 = torch.from_numpy(np.stack([gumbel_retained(cfg, g) for g in range(G)])).to(dev)
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t0
     print(f"# generated and uploaded {G} heads in {gen_s:.1f} s", file=sys.stderr, flush=True)
 
-    if cfg.removal is not None:
-        cap_list = [krs.uniform_capacity(N, cfg.removal)] * G
-    else:
-        cap_list = [int(c) for c in dirichlet_capacities(cfg)]
-    caps = torch.tensor(cap_list, dtype=torch.int32, device=dev)
-    offsets = krs.capacity_offsets(cap_list, N)
-    offsets_dev = krs.capacity_offsets_device(caps, N)
     s_out, sel_out, rep_out = {}, {}, {}
     s_ws = r_ws = None
+    if not repair_mode:
+        caps = torch.tensor(cap_list, dtype=torch.int32, device=dev)
+        offsets = krs.capacity_offsets(cap_list, N)
+        offsets_dev = krs.capacity_offsets_device(caps, N)
 
     def step(ev_s=None, ev_sel=None, ev_r=None):
         nonlocal s_ws, r_ws
-        r = krs.score(K, V, cfg.tau, cfg.window, cfg.sink, cfg.recent, out=s_out, ws=s_ws, events=ev_s)
-        s_ws = r["ws"]
-        s_out.update({k: r[k] for k in ("count", "best_sim", "best_idx", "energy", "score")})
-        sl = krs.select(r["score"], r["energy"], caps, cfg.sink, cfg.recent, out=sel_out, events=ev_sel,
-                        offsets=offsets_dev, total=int(offsets[-1]))
-        sel_out.update({"keep": sl["keep"], "kept_idx": sl["kept_idx"]})
-        rp = krs.repair(K, sl["keep"], cfg.tau, cfg.window, cfg.sink, cfg.recent, prior=r, out=rep_out, ws=r_ws,
-                        events=ev_r)
+        if repair_mode:
+            rp = krs.repair(K, S0, cfg.tau, cfg.window, cfg.sink, cfg.recent, out=rep_out, ws=r_ws, events=ev_r)
+        else:
+            r = krs.score(K, V, cfg.tau, cfg.window, cfg.sink, cfg.recent, out=s_out, ws=s_ws, events=ev_s)
+            s_ws = r["ws"]
+            s_out.update({k: r[k] for k in ("count", "best_sim", "best_idx", "energy", "score")})
+            sl = krs.select(r["score"], r["energy"], caps, cfg.sink, cfg.recent, out=sel_out, events=ev_sel,
+                            offsets=offsets_dev, total=int(offsets[-1]))
+            sel_out.update({"keep": sl["keep"], "kept_idx": sl["kept_idx"]})
+            rp = krs.repair(K, sl["keep"], cfg.tau, cfg.window, cfg.sink, cfg.recent, prior=r, out=rep_out,
+                            ws=r_ws, events=ev_r)
         r_ws = rp["ws"]
         rep_out.update({k: rp[k] for k in ("keep", "best_sim", "best_idx", "n_orphans", "n_donors", "n_swaps",
                                            "pairs")})
@@ -199,11 +281,14 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [(krs.Events(3), krs.Events(2), krs.Events(5)) for _ in range(args.steps)]
+    evs = [(krs.Events(4), krs.Events(2), krs.Events(5)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(*evs[k])
+        if repair_mode:
+            step(ev_r=evs[k][2])
+        else:
+            step(*evs[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
@@ -211,103 +296,76 @@ def main():
     def avg(fn):
         return float(np.mean([fn(e) for e in evs]))
 
-    norms_ms = avg(lambda e: e[0].elapsed_ms(0, 1))
-    gram_ms = avg(lambda e: e[0].elapsed_ms(1, 2))
-    select_ms = avg(lambda e: e[1].elapsed_ms(0, 1))
-    r_norms_ms = avg(lambda e: e[2].elapsed_ms(0, 1))
-    r_compact_ms = avg(lambda e: e[2].elapsed_ms(1, 2))
-    r_gram_ms = avg(lambda e: e[2].elapsed_ms(2, 3))
-    r_swap_ms = avg(lambda e: e[2].elapsed_ms(3, 4))
+    phases = {}
+    if not repair_mode:
+        phases["norms_energy"] = avg(lambda e: e[0].elapsed_ms(0, 1))
+        phases["gram_score"] = avg(lambda e: e[0].elapsed_ms(1, 2))
+        phases["score_resolve"] = avg(lambda e: e[0].elapsed_ms(2, 3))
+        phases["select"] = avg(lambda e: e[1].elapsed_ms(0, 1))
+    phases["repair_norms"] = avg(lambda e: e[2].elapsed_ms(0, 1))
+    phases["repair_compact"] = avg(lambda e: e[2].elapsed_ms(1, 2))
+    phases["repair_gram"] = avg(lambda e: e[2].elapsed_ms(2, 3))
+    phases["repair_swap"] = avg(lambda e: e[2].elapsed_ms(3, 4))
     for e in evs:
         for x in e:
             x.close()
 
-    # packed cache of the last step's selection (not part of the timed step)
-    gev = [krs.Events(2) for _ in range(args.steps)]
+    # retained-set sizes of the repair's input, and the rows its sweep visits
+    if repair_mode:
+        kept_in = S0.sum(1, dtype=torch.int64).cpu().numpy()
+        swept_frac = 1.0
+    else:
+        kept_in = np.asarray(cap_list, dtype=np.int64)
+        bi = s_out["best_idx"].long()
+        reused = (bi < 0) | torch.gather(sel_out["keep"], 1, bi.clamp(min=0)).bool()
+        swept_frac = 1.0 - reused.float().mean().item()
+    rgram = float(sum(2.0 * N * int(k) * d for k in kept_in))  # every row against the retained columns
+
+    # packed cache of the last step's retained set S1 (not part of the timed step)
+    s1_counts = rep_out["keep"].sum(1, dtype=torch.int32)
+    s1_total = int(kept_in.sum())  # repair keeps each head's budget
+    s1_off = krs.capacity_offsets_device(s1_counts, N)
+    s1_sel = krs.select(rep_out["keep"].double(), rep_out["keep"].double(), s1_counts, 0, 0, offsets=s1_off,
+                        total=s1_total)  # S1's positions in order: every kept entry scores 1, the rest 0
     gout = {}
-    for k in range(args.steps + 1):
-        gres = krs.gather_kv(K, V, sel_out["kept_idx"], offsets_dev, total=int(offsets[-1]), out=gout,
-                             events=gev[k - 1] if k else None)
-        gout = {"keys": gres["keys"], "values": gres["values"]}
-    torch.cuda.synchronize()
-    gather_ms = float(np.mean([e.elapsed_ms(0, 1) for e in gev]))
-    for e in gev:
-        e.close()
-    gather_rows = gres["total"]
-    gather_bytes = gather_rows * (8 * d + 4)
 
-    # score-variant keys (permuted counts, seed 11) for the last step's counts
-    from synth import count_permutation
-    permd = torch.from_numpy(np.stack([count_permutation(cfg, g, cap_list[g], 11) for g in range(G)])).to(dev)
-    vev = [krs.Events(2) for _ in range(args.steps)]
-    vout = {}
-    for k in range(args.steps + 1):
-        vres = krs.variant_score(s_out["count"], s_out["energy"], "twin", perm=permd, out=vout,
-                                 events=vev[k - 1] if k else None)
-        vout = vres
-    torch.cuda.synchronize()
-    variant_ms = float(np.mean([e.elapsed_ms(0, 1) for e in vev]))
-    for e in vev:
-        e.close()
-    variant_bytes = G * N * (4 + 8 + 4 + 4 + 16)  # perm, energy, own and permuted count, score and tie
-    del permd, vout, vres
+    def gather(ev):
+        nonlocal gout
+        r = krs.gather_kv(K, V, s1_sel["kept_idx"], s1_off, total=s1_total, out=gout, events=ev)
+        gout = {"keys": r["keys"], "values": r["values"]}
+        return r
 
-    # count statistics of the last step (Twin selection vs value-only selection)
-    vsel = krs.select(s_out["energy"], s_out["energy"], caps, cfg.sink, cfg.recent, offsets=offsets)
-    sev = [krs.Events(2) for _ in range(args.steps)]
-    for k in range(args.steps + 1):
-        sres = krs.count_stats(s_out["count"], s_out["energy"], caps, cfg.sink, cfg.recent,
-                               keep_twin=sel_out["keep"], keep_value=vsel["keep"], events=sev[k - 1] if k else None)
-    torch.cuda.synchronize()
-    stats_ms = float(np.mean([e.elapsed_ms(0, 1) for e in sev]))
-    for e in sev:
-        e.close()
-    st_np = sres["stats"].cpu().numpy()
-    stats_bytes = G * N * (4 + 8 + 1 + 1) * 2  # count, energy and both masks, read twice
-    del vsel
+    gres, (gather_ms,) = _timed(gather, args.steps, 2, krs)
+    gather_bytes = gres["total"] * ((8 if V is not None else 4) * d + 4)
+    del s1_sel, gout
 
-    # per-head capacities from prefix attention, 8 KV heads per layer
-    # (not part of the timed step)
-    from synth import make_queries
-    Qh = torch.from_numpy(np.stack([make_queries(cfg, g) for g in range(G)]).view(np.int16)).to(dev)
-    Hkv = 8 if G % 8 == 0 else 1
-    B_alloc = krs.uniform_capacity(N, cfg.removal if cfg.removal is not None else 0.5)
-    aev = [krs.Events(4) for _ in range(args.steps)]
-    aout, aws = {}, None
-    for k in range(args.steps + 1):
-        ares = krs.allocate(K, Qh, Hkv, B_alloc, cfg.sink, cfg.recent, out=aout, ws=aws,
-                            events=aev[k - 1] if k else None)
-        aws = ares["ws"]
-        aout = {kk: ares[kk] for kk in ("capacity", "g_count", "z")}
-    torch.cuda.synchronize()
-    alloc_ms = [float(np.mean([e.elapsed_ms(a, a + 1) for e in aev])) for a in range(3)]
-    for e in aev:
-        e.close()
-    nq = Qh.shape[1] * Qh.shape[2]
-    logit_flops = 2.0 * G * nq * N * d  # one fp64 dot product per (query, key)
-    del Qh
+    extras = {}
+    if not repair_mode:
+        extras = _score_extras(cfg, args, krs, torch, dev, K, s_out, sel_out, caps, cap_list, offsets_dev, offsets)
 
-    alg = algorithmic_gram_flops(N, d, cfg.window, G)
-    dense = 2.0 * G * N * N * d
-    achieved = alg / (gram_ms * 1e-3) / 1e12
-    exec_tflops = dense / (gram_ms * 1e-3) / 1e12
-    mean_cap = float(np.mean(cap_list))
-    rgram = restricted_gram_flops(N, mean_cap, d, G)
-    # rows the restricted sweep visits: those whose unrestricted best twin
-    # (the prior from the score pass) was not retained
-    bi = s_out["best_idx"].long()
-    reused = (bi < 0) | torch.gather(sel_out["keep"], 1, bi.clamp(min=0)).bool()
-    swept_frac = 1.0 - reused.float().mean().item()
-    norms_bytes = G * N * (4 * d + 20)
+    if repair_mode:
+        dom_ms = phases["repair_gram"]
+        alg = rgram
+        kernel = f"gram_kernel<{REPAIR_SHAPE[d]}, repair>"
+    else:
+        dom_ms = phases["gram_score"]
+        alg = algorithmic_gram_flops(N, d, cfg.window, G)
+        kernel = f"gram_kernel<{SCORE_SHAPE[d]}, score>"
+    achieved = alg / (dom_ms * 1e-3) / 1e12
 
     traffic = None
     meas = MEASURED_TRAFFIC.get(source_hash(GRAM_SOURCE))
-    if meas is not None and meas.get("workload") == (G, N, d):
+    if meas is not None and meas.get("workload") == (G, N, d) and meas.get("kernel") == kernel:
         traffic = meas["bytes_per_launch"]
 
     twin = int(round(cfg.twin_frac * 100))
-    budget = (f"{int(round(cfg.removal * 100))}% removal" if cfg.removal is not None
-              else f"Dirichlet(1) split of a {int(round(cfg.budget_frac * 100))}% budget per group of {cfg.group} heads")
+    if repair_mode:
+        budget = "repair of the top half by a random per-token Gumbel score (no score pass, no prior)"
+    elif cfg.removal is not None:
+        budget = f"{int(round(cfg.removal * 100))}% removal; score + select + repair of the selected set"
+    else:
+        budget = (f"Dirichlet(1) split of a {int(round(cfg.budget_frac * 100))}% budget per group of {cfg.group} "
+                  f"heads; score + select + repair of the selected set")
     line = {
         "metric": METRIC,
         "value": G * N / (ms_per_step * 1e-3),
@@ -322,24 +380,85 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {G} heads x N={N} x d={d}, {twin}% planted twins, tau {cfg.tau}, "
-                               f"window {cfg.window}, {budget}; score + select + repair of the selected set",
+                               f"window {cfg.window}, {budget}",
                    "G": G, "N": N, "d": d, "tau": cfg.tau, "window": cfg.window, "sink": cfg.sink,
-                   "recent": cfg.recent, "mean_capacity": mean_cap, "parallelism": "single GPU"},
+                   "recent": cfg.recent, "mean_retained": float(np.mean(kept_in)), "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "kernel": f"gram_kernel<{SCORE_SHAPE[d]}, score>", "algorithmic_flop_per_launch": alg,
-                     "avg_launch_ms": gram_ms},
-        "gram": {"dense_equiv_tflops": exec_tflops, "mfma_frac_dense_equiv": exec_tflops / PEAK_BF16_TFLOPS,
-                 "keys_per_s": G * N / (gram_ms * 1e-3), "ms": gram_ms},
-        "phases_ms": {"norms_energy": norms_ms, "gram_score": gram_ms, "select": select_ms,
-                      "repair_norms": r_norms_ms, "repair_compact": r_compact_ms, "repair_gram": r_gram_ms,
-                      "repair_swap": r_swap_ms},
-        "phase_rates": {"norms_energy_GBs": norms_bytes / (norms_ms * 1e-3) / 1e9,
-                        "repair_gram_dense_tflops": rgram * swept_frac / (r_gram_ms * 1e-3) / 1e12,
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": kernel,
+                     "algorithmic_flop_per_launch": alg, "avg_launch_ms": dom_ms},
+        "phases_ms": phases,
+        "phase_rates": {"repair_gram_tflops_on_swept_rows": rgram * swept_frac / (phases["repair_gram"] * 1e-3) / 1e12,
                         "repair_rows_swept_frac": swept_frac},
-        "gather_kv": {"ms": gather_ms, "rows": gather_rows, "algorithmic_bytes": gather_bytes,
+        "gather_kv": {"ms": gather_ms, "rows": gres["total"], "algorithmic_bytes": gather_bytes,
                       "GBs": gather_bytes / (gather_ms * 1e-3) / 1e9,
                       "frac_hbm": gather_bytes / (gather_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "swaps_total": int(rep_out["n_swaps"].sum().item()),
+        "generation_s": gen_s,
+    }
+    if not repair_mode:
+        dense = 2.0 * G * N * N * d
+        line["gram"] = {"dense_equiv_tflops": dense / (dom_ms * 1e-3) / 1e12,
+                        "mfma_frac_dense_equiv": dense / (dom_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                        "keys_per_s": G * N / (dom_ms * 1e-3), "ms": dom_ms}
+        norms_bytes = G * N * (4 * d + 20)
+        line["phase_rates"]["norms_energy_GBs"] = norms_bytes / (phases["norms_energy"] * 1e-3) / 1e9
+        line.update(extras)
+    if cpu is not None:
+        line["cpu_baseline"] = {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    print(json.dumps(line), flush=True)
+    if args.results_dir:
+        os.makedirs(args.results_dir, exist_ok=True)
+        with open(os.path.join(args.results_dir, f"{cfg.name}.bench.json"), "w") as f:
+            json.dump(line, f, indent=1)
+
+
+def _score_extras(cfg, args, krs, torch, dev, K, s_out, sel_out, caps, cap_list, offsets_dev, offsets):
+    """Untimed-step extras of the score workloads: permuted-count variant
+    keys, count statistics, head allocation."""
+    G, N, d = cfg.G, cfg.N, cfg.d
+    from synth import count_permutation, make_queries
+
+    permd = torch.from_numpy(np.stack([count_permutation(cfg, g, cap_list[g], 11) for g in range(G)])).to(dev)
+    vout = {}
+
+    def variant(ev):
+        nonlocal vout
+        vout = krs.variant_score(s_out["count"], s_out["energy"], "twin", perm=permd, out=vout, events=ev)
+        return vout
+
+    _, (variant_ms,) = _timed(variant, args.steps, 2, krs)
+    variant_bytes = G * N * (4 + 8 + 4 + 4 + 16)  # perm, energy, own and permuted count, score and tie
+    del permd, vout
+
+    vsel = krs.select(s_out["energy"], s_out["energy"], caps, cfg.sink, cfg.recent, offsets=offsets_dev,
+                      total=int(offsets[-1]))
+
+    def stats(ev):
+        return krs.count_stats(s_out["count"], s_out["energy"], caps, cfg.sink, cfg.recent,
+                               keep_twin=sel_out["keep"], keep_value=vsel["keep"], events=ev)
+
+    sres, (stats_ms,) = _timed(stats, args.steps, 2, krs)
+    st_np = sres["stats"].cpu().numpy()
+    stats_bytes = G * N * (4 + 8 + 1 + 1) * 2  # count, energy and both masks, read twice
+    del vsel
+
+    Qh = torch.from_numpy(np.stack([make_queries(cfg, g) for g in range(G)]).view(np.int16)).to(dev)
+    Hkv = 8 if G % 8 == 0 else 1
+    B_alloc = krs.uniform_capacity(N, cfg.removal if cfg.removal is not None else 0.5)
+    aout, aws = {}, None
+
+    def alloc(ev):
+        nonlocal aout, aws
+        r = krs.allocate(K, Qh, Hkv, B_alloc, cfg.sink, cfg.recent, out=aout, ws=aws, events=ev)
+        aws = r["ws"]
+        aout = {kk: r[kk] for kk in ("capacity", "g_count", "z")}
+        return r
+
+    _, alloc_ms = _timed(alloc, args.steps, 4, krs)
+    nq = Qh.shape[1] * Qh.shape[2]
+    logit_flops = 2.0 * G * nq * N * d  # one fp64 dot product per (query, key)
+    del Qh, aws
+    return {
         "variant_score": {"ms": variant_ms, "variant": "twin with permuted counts (seed 11)",
                           "GBs": variant_bytes / (variant_ms * 1e-3) / 1e9,
                           "frac_hbm": variant_bytes / (variant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
@@ -350,12 +469,7 @@ def main():
                      "rank_eq5_ms": alloc_ms[2], "heads_per_layer": Hkv, "queries_per_head": nq,
                      "logit_fp64_tflops": logit_flops / (alloc_ms[0] * 1e-3) / 1e12,
                      "frac_fp64_peak": logit_flops / (alloc_ms[0] * 1e-3) / 1e12 / PEAK_FP64_TFLOPS},
-        "swaps_total": int(rep_out["n_swaps"].sum().item()),
-        "generation_s": gen_s,
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, cap_list)
-    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -77,7 +77,7 @@ typedef enum twinkv_status {
   TWINKV_ERR_UNSUPPORTED = -2, /* head dim other than 64 or 128                        */
   TWINKV_ERR_WORKSPACE = -3,   /* workspace smaller than twinkv_workspace_bytes()       */
   TWINKV_ERR_HIP = -4,         /* the HIP runtime refused a launch or an event record   */
-  TWINKV_ERR_TOO_LARGE = -5    /* G*N beyond the static scratch of twinkv_score_noalloc */
+  TWINKV_ERR_TOO_LARGE = -5    /* workspace beyond the static scratch of twinkv_score_noalloc */
 } twinkv_status;
 
 /* Problem description shared by all entry points. */
@@ -96,7 +96,7 @@ typedef struct twinkv_params {
 enum { TWINKV_OP_SCORE = 0, TWINKV_OP_SELECT = 1, TWINKV_OP_REPAIR = 2 };
 
 /* Phase counts for the `marks` argument. */
-enum { TWINKV_SCORE_PHASES = 2, TWINKV_SELECT_PHASES = 1, TWINKV_REPAIR_PHASES = 4, TWINKV_GATHER_PHASES = 1,
+enum { TWINKV_SCORE_PHASES = 3, TWINKV_SELECT_PHASES = 1, TWINKV_REPAIR_PHASES = 4, TWINKV_GATHER_PHASES = 1,
        TWINKV_ALLOC_PHASES = 3, TWINKV_VARIANT_PHASES = 1, TWINKV_STATS_PHASES = 1 };
 
 /* Number of int64 counts per head written by twinkv_count_stats. */
@@ -135,7 +135,14 @@ const char* twinkv_status_string(int status);
  * Protected positions take part in the counts ([P2] 3.2).
  * keys, values: bf16 [G][N][d].  count, best_idx: int32 [G][N].
  * best_sim, energy, score, omega: double [G][N].
- * Phases for `marks`: 0 = norms and energies, 1 = fused Gram, fixup and score.
+ * Each unordered nonlocal pair is evaluated once (on the MFMA matrix cores,
+ * bf16 products exact, fp32 sums); the chosen best twin is then recomputed
+ * in fp64.  The workspace grows with N: about 48 bytes per key plus
+ * 2 bytes * N / 384 (d = 64) or N / 256 (d = 128) per key for the column
+ * maxima of each row block.
+ * Phases for `marks`: 0 = norms and energies, 1 = single-order Gram sweep
+ * (counts, row-side best twin, column maxima), 2 = resolve (exact column-side
+ * best twin, outputs and scores).
  */
 int twinkv_score(const twinkv_params* params, const void* keys, const void* values,
                  int32_t* count, double* best_sim, int32_t* best_idx, double* energy,
@@ -146,11 +153,11 @@ int twinkv_score(const twinkv_params* params, const void* keys, const void* valu
  * twinkv_score_noalloc - twinkv_score for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): the same kernels and the same outputs,
- * bit for bit, with the norms pass's scratch (fp64 squared norms and fp32
- * inverse norms, 12 bytes per key) taken from a static device array of the
- * library instead of a workspace argument.  Neither this call nor the
- * library allocates or frees anything; the array, sized for
- * TWINKV_NOALLOC_MAX_KEYS keys (24 MiB), is part of the library's device
+ * bit for bit, with the workspace twinkv_score takes (squared and inverse
+ * norms, the sweep's column maxima, counters and candidate bits) carved from
+ * a static device array of the library instead.  Neither this call nor the
+ * library allocates or frees anything; the array,
+ * TWINKV_NOALLOC_SCRATCH_BYTES (64 MiB), is part of the library's device
  * code and each device it runs on holds its own copy until the process
  * ends.  The scratch used is the current device's (hipGetDevice), so
  * `stream` must belong to it; its address is looked up on the first call on
@@ -158,11 +165,13 @@ int twinkv_score(const twinkv_params* params, const void* keys, const void* valu
  * keeps the last call's contents (each call writes every entry it reads
  * before reading it): calls that overlap on one device, on different
  * streams or from different threads, race and give wrong results.
- * Arguments and outputs as twinkv_score; G*N > TWINKV_NOALLOC_MAX_KEYS
- * returns TWINKV_ERR_TOO_LARGE before anything is launched.
+ * Arguments and outputs as twinkv_score; a problem whose workspace
+ * (twinkv_workspace_bytes(TWINKV_OP_SCORE, params)) exceeds the array
+ * returns TWINKV_ERR_TOO_LARGE before anything is launched (at d = 64 that
+ * admits, e.g., 256 heads of N = 8192 or 32 heads of N = 32768).
  * Phases for `marks`: as twinkv_score.
  */
-enum { TWINKV_NOALLOC_MAX_KEYS = 1 << 21 };
+enum { TWINKV_NOALLOC_SCRATCH_BYTES = 64 << 20 };
 int twinkv_score_noalloc(const twinkv_params* params, const void* keys, const void* values, int32_t* count,
                          double* best_sim, int32_t* best_idx, double* energy, double* score, double* omega,
                          hipStream_t stream, hipEvent_t* marks);

@@ -20,9 +20,9 @@ LIB_PATH = os.path.join(_HERE, "libtwinkv.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "twinkv.h")
 
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5
-NOALLOC_MAX_KEYS = 1 << 21
+NOALLOC_SCRATCH_BYTES = 64 << 20
 OP_SCORE, OP_SELECT, OP_REPAIR = 0, 1, 2
-SCORE_PHASES, SELECT_PHASES, REPAIR_PHASES, GATHER_PHASES, ALLOC_PHASES, VARIANT_PHASES = 2, 1, 4, 1, 3, 1
+SCORE_PHASES, SELECT_PHASES, REPAIR_PHASES, GATHER_PHASES, ALLOC_PHASES, VARIANT_PHASES = 3, 1, 4, 1, 3, 1
 VARIANTS = {"twin": 0, "value": 1, "rarity": 2}
 STAT_INTS = 26
 STATS_PHASES = 1
@@ -246,7 +246,8 @@ def score(keys, values, tau, window, sink=4, recent=64, omega=False, out=None, w
 
 def score_noalloc(keys, values, tau, window, sink=4, recent=64, omega=False, out=None, events=None):
     """score() through twinkv_score_noalloc: the library's static per-device
-    scratch instead of a workspace (G*N at most NOALLOC_MAX_KEYS).  Output
+    scratch instead of a workspace (whose size must not exceed
+    NOALLOC_SCRATCH_BYTES).  Output
     tensors are allocated here unless given in ``out``; the library call
     itself allocates nothing.  Calls that overlap on one device race."""
     lib = load()

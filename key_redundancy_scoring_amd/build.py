@@ -21,7 +21,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libtwinkv.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "norms.hip", "gram.hip", "select.hip", "repair.hip", "gather.hip", "alloc.hip", "stats.hip"]
+SOURCES = ["api.hip", "norms.hip", "gram.hip", "tri.hip", "select.hip", "repair.hip", "gather.hip", "alloc.hip", "stats.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}",
@@ -39,7 +39,8 @@ COMMON = [
 # Gram sweep: MFMA results go straight to VGPRs, where the epilogue reads them,
 # instead of AGPRs that would need a copy per accumulator; its inputs are finite
 # (no NaN), so max trees need no NaN-quieting copies (infinities stay honoured).
-PER_SOURCE = {"gram.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
+PER_SOURCE = {"gram.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+              "tri.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
 
 
 def _hipcc() -> str:

@@ -54,9 +54,18 @@ struct Carve {
   }
 };
 
+// Score workspace: squared norms, inverse norms, then the single-order
+// sweep's column maxima, row-side results, column counts, packed best twins,
+// overall maxima and candidate bits (carved in this order by score_carve).
 size_t score_ws(const twinkv_params* p) {
-  const size_t n = (size_t)p->G * (size_t)p->N;
-  return align_up(n * sizeof(double)) + align_up(n * sizeof(float));
+  const size_t G = (size_t)p->G, N = (size_t)p->N;
+  const size_t n = G * N;
+  const int rows = tri_rows(p->d);
+  const size_t nb = (N + rows - 1) / rows;
+  const size_t words = (N + 31) / 32;
+  return align_up(n * sizeof(double)) + align_up(n * sizeof(float)) +
+         align_up(G * (size_t)tri_part_per_head(p->N, rows) * sizeof(int32_t)) + 3 * align_up(n * sizeof(int32_t)) +
+         align_up(n * sizeof(uint64_t)) + align_up(n * sizeof(float)) + align_up(G * nb * words * sizeof(uint32_t));
 }
 
 size_t repair_ws(const twinkv_params* p) {
@@ -128,45 +137,56 @@ int check_score_args(const twinkv_params* p, const void* keys, const void* value
   return TWINKV_OK;
 }
 
-// Norms pass, then the fused Gram sweep, over caller-checked arguments with
-// the squared norms and inverse norms at nsq and rinv.
+// Norms pass, then the single-order Gram sweep and its resolve kernels, over
+// caller-checked arguments, with the workspace at `base` (score_ws bytes).
 int score_launch(const twinkv_params* p, const void* keys, const void* values, int32_t* count, double* best_sim,
-                 int32_t* best_idx, double* energy, double* score, double* omega, double* nsq, float* rinv,
-                 hipStream_t stream, hipEvent_t* marks) {
-  const size_t n = (size_t)p->G * (size_t)p->N;
+                 int32_t* best_idx, double* energy, double* score, double* omega, char* base, hipStream_t stream,
+                 hipEvent_t* marks) {
+  const size_t G = (size_t)p->G, N = (size_t)p->N;
+  const size_t n = G * N;
+  const int rows = tri_rows(p->d);
+  Carve cv{base};
+  double* nsq = cv.take<double>(n);
+  float* rinv = cv.take<float>(n);
+  TriArgs t{};
+  t.part = cv.take<int32_t>(G * (size_t)tri_part_per_head(p->N, rows));
+  t.rowcos = cv.take<float>(n);
+  t.rcount = cv.take<int32_t>(n);
+  t.ccount = cv.take<int32_t>(n);
+  t.best64 = cv.take<uint64_t>(n);
+  t.colmax = cv.take<float>(n);
+  t.nb = (p->N + rows - 1) / rows;
+  t.words = (p->N + 31) / 32;
+  t.cbits = cv.take<uint32_t>(G * (size_t)t.nb * (size_t)t.words);
   TRY(record(marks, 0, stream));
   TRY_HIP(launch_norms(static_cast<const uint16_t*>(keys), static_cast<const uint16_t*>(values), (int64_t)n, p->d,
                        nsq, rinv, energy, stream));
   TRY(record(marks, 1, stream));
-  GramArgs ga{};
-  ga.keys = static_cast<const uint16_t*>(keys);
-  ga.nsq = nsq;
-  ga.col_keys = ga.keys;
-  ga.col_rinv = rinv;
-  ga.energy = energy;
-  ga.G = p->G;
-  ga.N = p->N;
-  ga.d = p->d;
-  ga.window = kernel_window(p);
-  ga.tau = p->tau;
-  ga.count = count;
-  ga.best_sim = best_sim;
-  ga.best_idx = best_idx;
-  ga.score = score;
-  ga.omega = omega;
-  TRY_HIP(launch_gram(ga, GRAM_SCORE, stream));
-  TRY(record(marks, 2, stream));
+  t.keys = static_cast<const uint16_t*>(keys);
+  t.nsq = nsq;
+  t.rinv = rinv;
+  t.energy = energy;
+  t.G = p->G;
+  t.N = p->N;
+  t.d = p->d;
+  t.window = kernel_window(p);
+  t.tau = p->tau;
+  t.count = count;
+  t.best_sim = best_sim;
+  t.best_idx = best_idx;
+  t.score = score;
+  t.omega = omega;
+  TRY_HIP(launch_tri(t, stream, marks ? marks[2] : nullptr));
+  TRY(record(marks, 3, stream));
   return TWINKV_OK;
 }
 
-// Scratch of twinkv_score_noalloc: the squared norms (fp64) and inverse
-// norms (fp32) of up to TWINKV_NOALLOC_MAX_KEYS keys, carved like a score
-// workspace.  Each device the library runs on holds its own copy for the
+// Scratch of twinkv_score_noalloc: TWINKV_NOALLOC_SCRATCH_BYTES carved like
+// a score workspace.  Each device the library runs on holds its own copy for the
 // life of the process.  In host code `scratch` names a host-side stand-in,
 // never the device memory: its device address is looked up once per device
 // with hipGetSymbolAddress and only that address is handed to kernels.
-constexpr size_t kScratchBytes =
-    align_up((size_t)TWINKV_NOALLOC_MAX_KEYS * sizeof(double)) + align_up((size_t)TWINKV_NOALLOC_MAX_KEYS * sizeof(float));
+constexpr size_t kScratchBytes = TWINKV_NOALLOC_SCRATCH_BYTES;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
@@ -200,7 +220,7 @@ const char* twinkv_status_string(int status) {
     case TWINKV_ERR_UNSUPPORTED: return "unsupported head dimension (64 or 128 only)";
     case TWINKV_ERR_WORKSPACE: return "workspace too small";
     case TWINKV_ERR_HIP: return "HIP runtime error";
-    case TWINKV_ERR_TOO_LARGE: return "problem larger than the static scratch (G*N > TWINKV_NOALLOC_MAX_KEYS)";
+    case TWINKV_ERR_TOO_LARGE: return "problem larger than the static scratch (workspace > TWINKV_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -267,27 +287,20 @@ int twinkv_score(const twinkv_params* p, const void* keys, const void* values, i
   const size_t need = score_ws(p);
   if (!workspace || workspace_bytes < need) return TWINKV_ERR_WORKSPACE;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return TWINKV_ERR_ARG;
-  Carve cv{static_cast<char*>(workspace)};
-  const size_t n = (size_t)p->G * (size_t)p->N;
-  double* nsq = cv.take<double>(n);
-  float* rinv = cv.take<float>(n);
-  return score_launch(p, keys, values, count, best_sim, best_idx, energy, score, omega, nsq, rinv, stream, marks);
+  return score_launch(p, keys, values, count, best_sim, best_idx, energy, score, omega,
+                      static_cast<char*>(workspace), stream, marks);
 }
 
 int twinkv_score_noalloc(const twinkv_params* p, const void* keys, const void* values, int32_t* count,
                          double* best_sim, int32_t* best_idx, double* energy, double* score, double* omega,
                          hipStream_t stream, hipEvent_t* marks) {
   TRY(check_score_args(p, keys, values, count, best_sim, best_idx, energy, score));
-  if (p->G * p->N > TWINKV_NOALLOC_MAX_KEYS) return TWINKV_ERR_TOO_LARGE;
+  if (score_ws(p) > kScratchBytes) return TWINKV_ERR_TOO_LARGE;
   char* base = nullptr;
   TRY(scratch_of_current_device(&base));
-  // the same carving as a workspace: nsq, then rinv, each 256-byte aligned;
-  // the norms pass writes every entry the sweep reads, so nothing is cleared
-  Carve cv{base};
-  const size_t n = (size_t)p->G * (size_t)p->N;
-  double* nsq = cv.take<double>(n);
-  float* rinv = cv.take<float>(n);
-  return score_launch(p, keys, values, count, best_sim, best_idx, energy, score, omega, nsq, rinv, stream, marks);
+  // the same carving as a workspace; every entry a kernel reads is written
+  // earlier in the same call (the clear kernel zeroes the counters)
+  return score_launch(p, keys, values, count, best_sim, best_idx, energy, score, omega, base, stream, marks);
 }
 
 int twinkv_capacity_offsets(const int32_t* capacity, int64_t G, int64_t N, int64_t* kept_off, hipStream_t stream) {

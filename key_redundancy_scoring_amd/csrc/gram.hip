@@ -57,7 +57,7 @@
 //     sweep its key stream together out of one L2.
 #include <limits.h>
 
-#include "internal.h"
+#include "sweep.h"
 
 #ifndef TWINKV_GRAM64_RB
 #define TWINKV_GRAM64_RB 4
@@ -78,26 +78,9 @@
 #define TWINKV_GRAM128_SC 128
 #endif
 
-#define TWINKV_LDS __attribute__((address_space(3)))
-#define TWINKV_GLOBAL __attribute__((address_space(1)))
-#define TWINKV_INLINE __attribute__((always_inline))
-
 namespace twinkv {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// Launch shape of the sweep: head dim, row blocks of 32 per wave, waves per
-// workgroup, columns per LDS stage, and waves per SIMD the registers are
-// budgeted for (two stage buffers of SC columns per workgroup must fit the
-// CU's LDS that many times over).
-template <int D_, int RB_, int WAVES_, int SC_, int OCC_>
-struct GramShape {
-  static constexpr int D = D_, RB = RB_, WAVES = WAVES_, SC = SC_, OCC = OCC_;
-  static constexpr int ROWS = WAVES * RB * 32;
-};
 // score mode at d = 64: four row blocks per wave, so each staged column
 // feeds 128 rows of the wave; about 240 VGPRs, two waves per SIMD
 using Shape64 = GramShape<64, TWINKV_GRAM64_RB, TWINKV_GRAM64_WAVES, TWINKV_GRAM64_SC, 2>;
@@ -108,63 +91,6 @@ using Shape64 = GramShape<64, TWINKV_GRAM64_RB, TWINKV_GRAM64_WAVES, TWINKV_GRAM
 // four row blocks pays
 using Shape64Short = GramShape<64, 2, 4, 128, 3>;
 using Shape128 = GramShape<128, TWINKV_GRAM128_RB, TWINKV_GRAM128_WAVES, TWINKV_GRAM128_SC, 2>;
-
-// vmcnt(0), other counters untouched (gfx9 s_waitcnt encoding)
-constexpr unsigned kWaitVm0 = 0x0F70;
-
-// One stage buffer: column keys (swizzled 16-byte chunks), inverse norms and
-// positions (repair mode).
-template <int D, int SC>
-struct Stage {
-  uint4 keys[SC * (D / 8)];
-  float rinv[SC];
-  int32_t pos[SC];
-};
-
-__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const TWINKV_GLOBAL void*)src, (TWINKV_LDS void*)lds_wave_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const TWINKV_GLOBAL void*)src, (TWINKV_LDS void*)lds_wave_base, 4, 0, 0);
-}
-
-__device__ __forceinline__ float max3f(float a, float b, float c) { return __builtin_fmaxf(a, __builtin_fmaxf(b, c)); }
-
-__device__ __forceinline__ float max16(const float* y) {
-  const float m01 = max3f(y[0], y[1], y[2]);
-  const float m02 = max3f(y[3], y[4], y[5]);
-  const float m03 = max3f(y[6], y[7], y[8]);
-  const float m04 = max3f(y[9], y[10], y[11]);
-  const float m05 = max3f(y[12], y[13], y[14]);
-  const float m11 = max3f(m01, m02, m03);
-  const float m12 = max3f(m04, m05, y[15]);
-  return __builtin_fmaxf(m11, m12);
-}
-
-__device__ __forceinline__ double dot8_exact(uint4 a, uint4 b) {
-  const uint32_t x[4] = {a.x, a.y, a.z, a.w};
-  const uint32_t y[4] = {b.x, b.y, b.z, b.w};
-  double s = 0.0;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    s += (double)(__uint_as_float(x[t] << 16) * __uint_as_float(y[t] << 16));
-    s += (double)(__uint_as_float(x[t] & 0xffff0000u) * __uint_as_float(y[t] & 0xffff0000u));
-  }
-  return s;
-}
-
-// XOR swizzle of the 16-byte chunks of stage column c (CH chunks per key).
-// Chunk k of column c lives at slot c*CH + (k ^ swz(c)).  For the A-operand
-// reads (lane l reads chunk k of column l mod 32) this puts any 8 consecutive
-// lanes on distinct 16-byte bank groups of a 128-byte row and any 16 on
-// distinct groups of a 256-byte row.
-template <int CH>
-__device__ __forceinline__ int swz(int c) {
-  return CH == 8 ? ((c ^ (c >> 3)) & 7) : (c & 15);
-}
-
-// column offset (within a 32-column tile) of accumulator r in half-wave h
-__device__ __forceinline__ int tile_col(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
 template <class S, int MODE>
 __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a) {

@@ -31,6 +31,47 @@ struct GramArgs {
   double* omega;          // score only, may be null
 };
 
+// Single-order score sweep (tri.hip).  Each unordered nonlocal pair is
+// computed once, in the workgroup of its lower position's row block: the
+// row side (the lower position's maximum over later columns) is tracked per
+// row as in the two-order sweep, the column side (each later position's
+// maximum over the block's rows) is reduced across lanes and stored per
+// (row block, column), and a resolve pass finds the exact best twin.
+struct TriArgs {
+  const uint16_t* keys;  // bf16 [G][N][d]
+  const double* nsq;     // ||k||^2 [G][N]
+  const float* rinv;     // 1/||k|| [G][N]
+  const double* energy;  // ||v||^2 [G][N]
+  int64_t G, N;
+  int32_t d, window;
+  double tau;
+  int64_t nb;            // row blocks per head
+  int64_t words;         // 32-bit candidate words per (head, row block): ceil(N/32)
+  // workspace
+  int32_t* part;         // column maxima per (head, row block), order-preserving fp32 bits; block rb
+                         // of head g holds columns rb*ROWS .. N-1 (see tri_part_offset)
+  float* rowcos;         // [G][N] fp32 row-side maximum cosine, -inf if none
+  int32_t* rcount;       // [G][N] row-side counts
+  int32_t* ccount;       // [G][N] column-side counts (cleared before the sweep)
+  uint64_t* best64;      // [G][N] packed (exact cosine, position) of the best twin found so far; 0 = none
+  float* colmax;         // [G][N] fp32 maximum cosine over both sides
+  uint32_t* cbits;       // [G][nb][words] candidate row blocks of each position (cleared before the sweep)
+  // outputs
+  int32_t* count;
+  double* best_sim;
+  int32_t* best_idx;
+  double* score;
+  double* omega;         // may be null
+};
+// Rows per row block of the single-order sweep at head dim d (64 or 128).
+int tri_rows(int d);
+// Entries of the column-maximum array per head.
+int64_t tri_part_per_head(int64_t N, int rows);
+// Clear, sweep, then resolve (column maxima, candidate blocks, exact column
+// side, final outputs).  `mark` (may be null) is recorded between the sweep
+// and the resolve kernels.
+hipError_t launch_tri(const TriArgs& a, hipStream_t stream, hipEvent_t mark);
+
 // nsq = ||k||^2 (fp64), rinv = 1/||k|| (fp32, 0 for a zero key) and energy =
 // ||v||^2 (fp64; skipped when values is null).
 hipError_t launch_norms(const uint16_t* keys, const uint16_t* values, int64_t nkeys, int d, double* nsq,

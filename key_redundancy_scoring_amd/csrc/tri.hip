@@ -1,0 +1,815 @@
+// Single-order score sweep: the nonlocal twin count c_i = #{ j : |i-j| > w,
+// sim(i,j) > tau } and the best nonlocal twin (b_i, a_i) of every position
+// ("TwinKV: A Composable Repair Pass ...", section 3.2, Eq. 1 and Eq. 2;
+// "Small Frequency Corrections ...", section 3.2), with every unordered
+// nonlocal pair {i, j} evaluated once, and the discounted score
+// e_i * ln((N+1)/(c_i+1)) ("Small Frequency Corrections ...", section 3.2).
+//
+// A pair i < j with j - i > w is evaluated in the workgroup that owns i's
+// row block, which sweeps the columns from its own first row to the end.
+// Its value serves both ends:
+//   * the row side (i's maximum over later j, the count of i) stays in the
+//     lane that holds row i, as in the two-order sweep: y = dot / ||k_j||,
+//     a 3-input max tree per 32x32 block and a running (maximum, first tile)
+//     per half-row;
+//   * the column side (j's maximum over the block's rows) is scaled to the
+//     cosine, merged over the wave's row blocks in each lane, then over the
+//     32 lanes that share a column set by a reduce-scatter of v_permlane16_swap
+//     and DPP row mirrors, then over the workgroup's waves in LDS, and stored
+//     per (row block, column); its counts are added atomically (rare: only
+//     when some element of a block crosses tau).
+// The resolve kernels then take, for every position, the largest of its row
+// side and of the column maxima of the row blocks before it, mark the
+// blocks whose maximum is within a margin of it, and re-sweep each such
+// block against just those positions to find the exact fp64 best twin.  The
+// row side's own best is made exact at the end of the sweep (the fused
+// fixup).  Both sides merge through a 64-bit atomic maximum of (exact
+// cosine, position) in which the low 30 bits of the order-preserving image
+// of the cosine carry the position, so equal cosines go to the lowest
+// position.  A workgroup sweeps two row blocks, rb and nb-1-rb, so every
+// workgroup covers about the same number of columns.
+#include <limits.h>
+
+#include "sweep.h"
+
+namespace twinkv {
+namespace {
+
+// d = 64: three row blocks of 32 per wave (96 rows), 384 rows per workgroup,
+// 256-column stages; 256 VGPRs at two waves per SIMD.  Four row blocks spill
+// with the column-side registers (and one wave per SIMD is slower).
+using TriShape64 = GramShape<64, 3, 4, 256, 2>;
+using TriShape128 = GramShape<128, 2, 4, 128, 2>;
+
+constexpr unsigned kDppMirror = 0x140;      // lane i of a 16-lane row reads lane 15 - i
+constexpr unsigned kDppHalfMirror = 0x141;  // lane i of an 8-lane half row reads lane 7 - i
+constexpr unsigned kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr unsigned kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr uint64_t kIdxMask = (1ull << 30) - 1;
+// screening margin in cosine units: far above the fp32 error of a dot product
+// of at most 128 exact bf16 products scaled by fp32 inverse norms (below 1e-5)
+constexpr float kMargin = 8e-5f;
+
+template <unsigned CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// The 16 accumulator values of a lane are 16 columns (tile_col(r, h)) for the
+// lane's row; the 32 lanes of a half-wave share those columns.  Returns, in
+// every lane, the maximum over its half-wave of column slot
+// 8*b1 + 4*b2 + 2*b3 + b4 (bk: bit k of the lane id); lanes l and l^1 agree.
+__device__ __forceinline__ float reduce_scatter16(const float (&v)[16]) {
+  const int l = threadIdx.x & 63;
+  float a[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    // rows of 16 lanes: odd rows of v[2k] swap with even rows of v[2k+1]
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[2 * k]), __float_as_uint(v[2 * k + 1]), false, false);
+    a[k] = __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  const bool b3 = (l >> 3) & 1, b2 = (l >> 2) & 1, b1 = (l >> 1) & 1;
+  float b[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float keep = b3 ? a[2 * m + 1] : a[2 * m];
+    const float send = b3 ? a[2 * m] : a[2 * m + 1];
+    b[m] = __builtin_fmaxf(keep, dpp<kDppMirror>(send));
+  }
+  float c[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const float keep = b2 ? b[2 * m + 1] : b[2 * m];
+    const float send = b2 ? b[2 * m] : b[2 * m + 1];
+    c[m] = __builtin_fmaxf(keep, dpp<kDppHalfMirror>(send));
+  }
+  const float keep = b1 ? c[1] : c[0];
+  const float send = b1 ? c[0] : c[1];
+  const float e = __builtin_fmaxf(keep, dpp<kDppXor2>(send));
+  return __builtin_fmaxf(e, dpp<kDppXor1>(e));
+}
+
+__device__ __forceinline__ int slot_of_lane(int lane) {
+  return 8 * ((lane >> 1) & 1) + 4 * ((lane >> 2) & 1) + 2 * ((lane >> 3) & 1) + ((lane >> 4) & 1);
+}
+
+// fp32 <-> int with the same order (for atomic maxima of signed values)
+__device__ __forceinline__ int ordered_f32(float v) {
+  const int b = __float_as_int(v + 0.0f);
+  return b >= 0 ? b : b ^ 0x7FFFFFFF;
+}
+__device__ __forceinline__ float unordered_f32(int o) { return __int_as_float(o >= 0 ? o : o ^ 0x7FFFFFFF); }
+
+// (exact cosine, position) -> one 64-bit key whose unsigned order is the
+// cosine's, then the lower position; 0 is below every key
+__device__ __forceinline__ uint64_t pack_best(double sim, int idx) {
+  uint64_t u = (uint64_t)__double_as_longlong(sim + 0.0);
+  u = (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+  return (u & ~kIdxMask) | (kIdxMask - (uint64_t)idx);
+}
+
+__device__ __forceinline__ int64_t part_offset(int64_t g, int64_t rb, int64_t N, int64_t nb, int rows) {
+  const int64_t per_head = nb * N - (int64_t)rows * nb * (nb - 1) / 2;
+  return g * per_head + rb * N - (int64_t)rows * rb * (rb - 1) / 2;
+}
+
+// Exact best of row i over the 16 columns of tile tp in half p (positions
+// j = tp*32 + tile_col(r, p), those with j < ncols and |i - j| > w): an fp32
+// screen, then fp64 for those within the margin of the largest.  Both lanes
+// of a row run it (each over the feature chunks 2s+h it holds) and combine
+// partial sums, so they reach identical results.  Positions map through
+// pos_of (identity in score mode).
+template <int D, class PosOf>
+__device__ __forceinline__ void exact_tile(const uint4* Kg, const double* nsq_g, const float* rinv_g, int i, double ni,
+                                           int tp, int p, int ncols, int w, int h, float margin, PosOf pos_of,
+                                           double& bb, int& aa) {
+  constexpr int CH = D / 8;
+  constexpr int KS = D / 16;
+  uint4 kr[KS];
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2) kr[s2] = Kg[(size_t)i * CH + 2 * s2 + h];
+  constexpr int BATCH = CH == 8 ? 4 : 2;
+  float ya[16];
+  float ymax = -__builtin_inff();
+#pragma unroll
+  for (int r0 = 0; r0 < 16; r0 += BATCH) {
+    uint4 q[BATCH][KS];
+    float rj[BATCH];
+    int jj[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int col = tp * 32 + tile_col(r0 + u, p);
+      const int cc = col < ncols ? col : ncols - 1;
+      const int j = pos_of(cc);
+      jj[u] = j;
+      const uint4* kj = Kg + (size_t)j * CH;
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) q[u][s2] = kj[2 * s2 + h];
+      rj[u] = rinv_g[j];
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int col = tp * 32 + tile_col(r0 + u, p);
+      const int j = jj[u];
+      const int dist = i > j ? i - j : j - i;
+      float part = 0.0f;
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) {
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[s2].x), __builtin_bit_cast(bf16x2, q[u][s2].x), part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[s2].y), __builtin_bit_cast(bf16x2, q[u][s2].y), part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[s2].z), __builtin_bit_cast(bf16x2, q[u][s2].z), part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[s2].w), __builtin_bit_cast(bf16x2, q[u][s2].w), part, false);
+      }
+      const float dotf = part + __shfl_xor(part, 32);
+      ya[r0 + u] = (col < ncols && dist > w) ? dotf * rj[u] : -__builtin_inff();
+      ymax = __builtin_fmaxf(ymax, ya[r0 + u]);
+    }
+  }
+  unsigned cm = 0u;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) cm |= (ya[r] > -__builtin_inff() && ya[r] >= ymax - margin) ? 1u << r : 0u;
+#pragma unroll 1
+  while (cm != 0u) {
+    const int r = __builtin_ctz(cm);
+    cm &= cm - 1u;
+    const int j = pos_of(tp * 32 + tile_col(r, p));
+    const uint4* kj = Kg + (size_t)j * CH;
+    double part = 0.0;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) part += dot8_exact(kr[s2], kj[2 * s2 + h]);
+    const double dot = part + __shfl_xor(part, 32);
+    const double nn = ni * nsq_g[j];
+    double sim = nn > 0.0 ? dot / sqrt(nn) : 0.0;
+    sim += 0.0;
+    if (aa < 0 || sim > bb || (sim == bb && j < aa)) {
+      bb = sim;
+      aa = j;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the sweep
+
+template <class S>
+__global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArgs a) {
+  constexpr int D = S::D;
+  constexpr int RB = S::RB;
+  constexpr int WAVES = S::WAVES;
+  constexpr int SC = S::SC;
+  constexpr int NT = 64 * WAVES;
+  constexpr int ROWS = S::ROWS;
+  constexpr int CH = D / 8;
+  constexpr int KS = D / 16;
+  constexpr int LOADS = SC * CH / NT;
+  constexpr int TILES = SC / 32;
+  static_assert(LOADS * NT == SC * CH, "stage load split");
+  static_assert(SC % 64 == 0 && SC / 64 <= WAVES, "stage columns: whole waves load rinv");
+  __shared__ StageK<D, SC> buf0;
+  __shared__ StageK<D, SC> buf1;
+  // per wave and stage column, the wave's column maximum; three buffers, so a
+  // stage's maxima are merged one barrier after its last tile was written
+  __shared__ float colpart[3][WAVES][SC];
+
+  const int64_t N = a.N;
+  const int64_t nb = a.nb;
+  const int64_t npair = (nb + 1) / 2;
+  const int64_t total = a.G * npair;
+  const int64_t per_xcd = (total + 7) / 8;
+  const int64_t logical = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (logical >= total) return;
+  const int64_t g = logical / npair;
+  const int64_t pidx = logical % npair;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int lrow = lane & 31;
+  const int w = a.window;
+  const uint4* Kg = reinterpret_cast<const uint4*>(a.keys) + (size_t)g * N * CH;
+  const float* rinv_g = a.rinv + (size_t)g * N;
+  const double* nsq_g = a.nsq + (size_t)g * N;
+  int32_t* ccount_g = a.ccount + (size_t)g * N;
+
+  // stage-load and A-operand offsets (see the two-order sweep)
+  static_assert((2 * NT / CH) % (CH == 8 ? 64 : 16) == 0 && 64 % (CH == 8 ? 64 : 16) == 0, "swizzle period");
+  uint32_t ld_off[2];
+  uint32_t a_off[2][KS];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int q = tid + NT * p;
+    const int c = q / CH;
+    ld_off[p] = (uint32_t)((c * CH + ((q % CH) ^ swz<CH>(c))) * 16 - p * NT * 16);
+    const int cp = 32 * p + lrow;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) a_off[p][s] = (uint32_t)((cp * CH + ((2 * s + h) ^ swz<CH>(cp))) * 16 - p * 32 * CH * 16);
+  }
+
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    const int64_t rb = pass == 0 ? pidx : nb - 1 - pidx;
+    if (pass == 1 && rb == pidx) break;  // the middle block of an odd count: once
+    const int col_start = (int)(rb * ROWS);
+    const int ncols = (int)N - col_start;  // this block sweeps columns col_start .. N-1
+    const int row0 = col_start + wave * (RB * 32);
+    int32_t* part_rb = a.part + part_offset(g, rb, N, nb, ROWS);
+
+    // ---- row keys (rows past the end repeat the last row: their values
+    // duplicate a real row's, so column maxima are unaffected; they count nothing)
+    bf16x8 brow[RB][KS];
+    float thr[RB], best[RB], rinvr[RB];
+    int btile[RB], cnt[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const int r = row0 + 32 * b + lrow;
+      const int i = r < N ? r : (int)N - 1;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) brow[b][s] = __builtin_bit_cast(bf16x8, Kg[(size_t)i * CH + 2 * s + h]);
+      const double ni = nsq_g[i];
+      // y = dot/||k_j|| is ||k_i|| cos, so cos > tau is y > tau*||k_i||; a zero
+      // key has cosine 0 with every key, which exceeds a negative tau; + 0.0f
+      // turns a -0 threshold into +0
+      thr[b] = r >= N ? __builtin_inff()
+                      : (ni == 0.0 && a.tau < 0.0) ? -__builtin_inff() : (float)(a.tau * sqrt(ni)) + 0.0f;
+      rinvr[b] = rinv_g[i];
+      best[b] = -__builtin_inff();
+      btile[b] = -1;
+      cnt[b] = 0;
+    }
+
+    const uint4* Cg = Kg + (size_t)col_start * CH;
+    const float* crinv = rinv_g + col_start;
+    auto issue = [&](int col0, StageK<D, SC>& sb) TWINKV_INLINE {
+      if (col0 + SC <= ncols) {
+        const char* base = reinterpret_cast<const char*>(Cg + (size_t)col0 * CH);
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) dma16(base + (size_t)NT * 16 * u + ld_off[u & 1], &sb.keys[NT * u + wave * 64]);
+        if (wave < SC / 64) dma4(crinv + col0 + tid, &sb.rinv[wave * 64]);
+        return;
+      }
+      const int lastc = ncols - 1;
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) {
+        const int c = col0 + tid / CH + (NT / CH) * u;
+        const int col = c < lastc ? c : lastc;
+        dma16(reinterpret_cast<const char*>(Cg + (size_t)col * CH) + (ld_off[u & 1] & (CH * 16 - 1)),
+              &sb.keys[NT * u + wave * 64]);
+      }
+      if (wave < SC / 64) {
+        const int col = col0 + tid < lastc ? col0 + tid : lastc;
+        dma4(crinv + col, &sb.rinv[wave * 64]);
+      }
+    };
+    auto load_a = [&](const StageK<D, SC>& sb, int tt, int par, bf16x8 (&A)[KS]) TWINKV_INLINE {
+      const char* kb = reinterpret_cast<const char*>(sb.keys) + tt * 32 * CH * 16;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + (par ? a_off[1][s] : a_off[0][s])));
+    };
+    auto load_rv = [&](const StageK<D, SC>& sb, int tt, float (&rv)[16]) TWINKV_INLINE {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const float4 r4 = *reinterpret_cast<const float4*>(&sb.rinv[tt * 32 + 8 * gq + 4 * h]);
+        rv[4 * gq + 0] = r4.x;
+        rv[4 * gq + 1] = r4.y;
+        rv[4 * gq + 2] = r4.z;
+        rv[4 * gq + 3] = r4.w;
+      }
+    };
+    // first and last row position of the wave (rows past the end clamped)
+    const int rlo = __builtin_amdgcn_readfirstlane(row0 < N ? row0 : (int)N - 1);
+    const int rhi = __builtin_amdgcn_readfirstlane(row0 + RB * 32 - 1 < N ? row0 + RB * 32 - 1 : (int)N - 1);
+    // bit tt: tile tt of stage st holds a pair with j - i <= w (or reaches the
+    // end); only tiles wholly past the band of every row of the wave are swept
+    auto masked_tiles = [&](int st) TWINKV_INLINE {
+      unsigned bits = 0;
+#pragma unroll
+      for (int tt = 0; tt < TILES; ++tt) {
+        const int c0 = col_start + (st * TILES + tt) * 32;
+        bits |= (unsigned)((c0 <= rhi + w) || (c0 + 31 >= (int)N)) << tt;
+      }
+      return bits;
+    };
+    auto tail_tiles = [&](int st) TWINKV_INLINE {
+      unsigned bits = 0;
+#pragma unroll
+      for (int tt = 0; tt < TILES; ++tt) bits |= (unsigned)(col_start + (st * TILES + tt) * 32 + 31 >= (int)N) << tt;
+      return bits;
+    };
+    // counts of y > tau*||k_i|| over the 16 values of block b: the row's, and
+    // (atomically, rare) each column's; (y > thr read off the sign of thr - y)
+    auto count16 = [&](const f32x16& y, int b) TWINKV_INLINE {
+      uint32_t c = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) c += __float_as_uint(thr[b] - y[r]) >> 31;
+      cnt[b] += (int)c;
+    };
+    auto colcount16 = [&](const f32x16& y, int b, int c0) TWINKV_INLINE {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (__float_as_uint(thr[b] - y[r]) >> 31) atomicAdd(&ccount_g[c0 + tile_col(r, h)], 1);
+    };
+    auto mfma_block = [&](const bf16x8 (&A)[KS], int b, f32x16& acc) TWINKV_INLINE {
+      acc = (f32x16){};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], brow[b][s], acc, 0, 0, 0);
+    };
+    float colmax[16];
+    // block b of a tile whose dots are in acc: y = dot/||k_j|| and its block
+    // maximum for the row side; z = y/||k_i|| (the cosine) merged into the
+    // column maxima over the wave's blocks
+    auto epilogue = [&](f32x16& acc, int b, const float (&rv)[16], bool live, int tile, int c0) TWINKV_INLINE {
+      float yy[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc[r] *= rv[r];
+        yy[r] = acc[r];
+      }
+      const float m = max16(yy);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float z = yy[r] * rinvr[b];
+        colmax[r] = (b == 0) ? z : __builtin_fmaxf(colmax[r], z);
+      }
+      if (live) {  // wave-uniform
+        btile[b] = m > best[b] ? tile : btile[b];
+        best[b] = __builtin_fmaxf(best[b], m);
+        if (__ballot(m > thr[b]) != 0ull) {
+          count16(acc, b);
+          colcount16(acc, b, c0);
+        }
+      }
+    };
+    const int slot = slot_of_lane(lane);
+    auto flush_cols = [&](int st, int tt, bool live) TWINKV_INLINE {
+      float v = reduce_scatter16(colmax);
+      if (!live) v = -__builtin_inff();  // a masked tile is added after the sweep
+      if ((lane & 1) == 0) colpart[st % 3][wave][tt * 32 + tile_col(slot, h)] = v;
+    };
+    auto merge_stage = [&](int st) TWINKV_INLINE {
+      for (int c = tid; c < SC; c += NT) {
+        const int col = st * SC + c;  // relative to col_start
+        if (col < ncols) {
+          float v = colpart[st % 3][0][c];
+#pragma unroll
+          for (int wv = 1; wv < WAVES; ++wv) v = __builtin_fmaxf(v, colpart[st % 3][wv][c]);
+          part_rb[col] = ordered_f32(v);
+        }
+      }
+    };
+    auto interleave = [&]() TWINKV_INLINE {
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // up to seven VALU
+      }
+    };
+
+    // ---- the sweep (the rolling pipeline of the two-order sweep)
+    const int nstages = (ncols + SC - 1) / SC;
+    const int tile0 = col_start >> 5;
+    f32x16 acc[RB];
+    bf16x8 A[KS];
+    float rv[16];
+    int band_lo = INT_MAX, band_hi = -1;  // masked tiles other than the tail (absolute tile ids)
+    if (nstages > 0) issue(0, buf0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    if (nstages > 1) issue(SC, buf1);
+    if (nstages > 0) {
+      load_a(buf0, 0, 0, A);
+#pragma unroll
+      for (int b = 0; b < RB; ++b) mfma_block(A, b, acc[b]);
+      load_rv(buf0, 0, rv);
+    }
+    auto stage = [&](int st, StageK<D, SC>& cur, const StageK<D, SC>& nxt) TWINKV_INLINE {
+      const unsigned mbits = __builtin_amdgcn_readfirstlane(masked_tiles(st));
+      const unsigned bbits = mbits & ~__builtin_amdgcn_readfirstlane(tail_tiles(st));
+      if (bbits != 0u) {
+        band_lo = min(band_lo, tile0 + st * TILES + __builtin_ctz(bbits));
+        band_hi = max(band_hi, tile0 + st * TILES + 31 - __builtin_clz(bbits));
+      }
+#pragma unroll 1
+      for (int tt = 0; tt < TILES - 1; ++tt) {
+        const int tile = tile0 + st * TILES + tt;
+        load_a(cur, tt + 1, (tt + 1) & 1, A);
+        const bool live = ((mbits >> tt) & 1u) == 0u;
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          epilogue(acc[b], b, rv, live, tile, tile * 32);
+          mfma_block(A, b, acc[b]);
+          interleave();
+        }
+        flush_cols(st, tt, live);
+        load_rv(cur, tt + 1, rv);
+      }
+      const bool more = st + 1 < nstages;
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      if (st >= 1) merge_stage(st - 1);
+      if (st + 2 < nstages) issue((st + 2) * SC, cur);
+      if (more) load_a(nxt, 0, 0, A);
+      const int tile = tile0 + st * TILES + TILES - 1;
+      const bool live = ((mbits >> (TILES - 1)) & 1u) == 0u;
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        epilogue(acc[b], b, rv, live, tile, tile * 32);
+        if (more) mfma_block(A, b, acc[b]);
+        interleave();
+      }
+      flush_cols(st, TILES - 1, live);
+      if (more) load_rv(nxt, 0, rv);
+    };
+#pragma unroll 1
+    for (int st = 0; st < nstages; st += 2) {
+      stage(st, buf0, buf1);
+      if (st + 1 >= nstages) break;
+      stage(st + 1, buf1, buf0);
+    }
+    __syncthreads();
+    if (nstages > 0) merge_stage(nstages - 1);
+    // every plain store of the column maxima is complete before the masked
+    // tiles add theirs atomically
+    __syncthreads();
+
+    // ---- masked tiles (the band range, the partial last tile), from global
+    // memory, with pairs j - i <= w, columns past the end and rows past the
+    // end excluded.  Tiles wholly on or below the band of every row are
+    // skipped.  An exact tie with the running maximum goes to the lower tile.
+    {
+      const int ntiles = tile0 + (ncols + 31) / 32;  // absolute end
+      const int last = ntiles - 1;
+      const int nband = band_hi >= 0 ? band_hi - band_lo + 1 : 0;
+      const bool last_extra = ncols > 0 && (ncols & 31) != 0 && !(nband > 0 && last >= band_lo && last <= band_hi);
+      const int nproc = nband + (last_extra ? 1 : 0);
+#pragma unroll 1
+      for (int k = 0; k < nproc; ++k) {
+        const int t = k < nband ? band_lo + k : last;
+        const int c0 = t * 32;
+        if (c0 + 31 <= rlo + w) continue;  // no pair of this tile has j - i > w (wave-uniform)
+        bf16x8 Am[KS];
+        {
+          const int c = c0 + lrow < N ? c0 + lrow : (int)N - 1;
+#pragma unroll
+          for (int s = 0; s < KS; ++s) Am[s] = __builtin_bit_cast(bf16x8, Kg[(size_t)c * CH + 2 * s + h]);
+        }
+        float rvm[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int col = c0 + tile_col(r, h);
+          rvm[r] = rinv_g[col < N ? col : N - 1];
+        }
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          f32x16 y;
+          mfma_block(Am, b, y);
+          const int i = row0 + 32 * b + lrow;
+          float yy[16];
+          int twins = 0;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int col = c0 + tile_col(r, h);
+            const bool ok = i < N && col < N && col - i > w;
+            yy[r] = ok ? y[r] * rvm[r] : -__builtin_inff();
+            const float z = ok ? yy[r] * rinvr[b] : -__builtin_inff();
+            colmax[r] = (b == 0) ? z : __builtin_fmaxf(colmax[r], z);
+            const bool tw = ok && yy[r] > thr[b];
+            twins += tw ? 1 : 0;
+            if (tw) atomicAdd(&ccount_g[col], 1);
+          }
+          cnt[b] += twins;
+          const float m = max16(yy);
+          if (m > best[b] || (m == best[b] && t < btile[b])) {
+            best[b] = m;
+            btile[b] = t;
+          }
+        }
+        const float v = reduce_scatter16(colmax);
+        const int col = c0 + tile_col(slot, h);
+        if ((lane & 1) == 0 && col < N && v > -__builtin_inff()) atomicMax(&part_rb[col - col_start], ordered_f32(v));
+      }
+    }
+
+    // ---- exact row side: per half-row, the fp32 maximum and its first tile;
+    // a half within the margin of the row's maximum is screened and its
+    // near-maximal columns recomputed in fp64
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const int i = row0 + 32 * b + lrow;
+      const bool row_ok = i < N;
+      const int ic = row_ok ? i : (int)N - 1;
+      double bb = -1.0;
+      int aa = -1;
+      const double ni = nsq_g[ic];
+      const float margin = 8e-5f * (float)sqrt(ni) + 1e-30f;  // y units (||k_i|| cos)
+      const float other = __shfl_xor(best[b], 32);
+      const bool look = row_ok && btile[b] >= 0 && best[b] >= other - margin;
+      const bool look_o = __shfl_xor((int)look, 32) != 0;
+      const int tile_o = __shfl_xor(btile[b], 32);
+      const bool look0 = (h == 0) ? look : look_o;
+      const bool look1 = (h == 1) ? look : look_o;
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps) {
+        const int p = (ps == 0 && look0) ? 0 : 1;
+        const bool lk = ps == 0 ? (look0 || look1) : (look0 && look1);
+        const int tp = (h == p) ? btile[b] : tile_o;
+        if (__ballot(lk) == 0ull) continue;
+        if (lk) exact_tile<D>(Kg, nsq_g, rinv_g, ic, ni, tp, p, (int)N, w, h, margin, [](int c) { return c; }, bb, aa);
+      }
+      const int c = cnt[b] + __shfl_xor(cnt[b], 32);
+      const float ymax = __builtin_fmaxf(best[b], __shfl_xor(best[b], 32));
+      if (h == 0 && row_ok) {
+        const size_t o = (size_t)g * N + i;
+        a.best64[o] = aa >= 0 ? pack_best(bb, aa) : 0ull;
+        a.rowcos[o] = ymax > -__builtin_inff() ? ymax * rinvr[b] : -__builtin_inff();
+        a.rcount[o] = c;
+      }
+    }
+    __syncthreads();  // LDS is reused by the next pass
+  }
+}
+
+// ---------------------------------------------------------------------------
+// resolve: the largest of each position's row side and column maxima, and
+// the row blocks within the margin of it
+
+template <int ROWS>
+__global__ __launch_bounds__(256) void tri_colmax_kernel(TriArgs a) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= a.G * a.N) return;
+  const int64_t N = a.N;
+  const int64_t g = q / N;
+  const int64_t k = q % N;
+  const int64_t rbk = k / ROWS;  // row blocks 0..rbk swept column k
+  float m = a.rowcos[q];
+  for (int64_t rb = 0; rb <= rbk; ++rb)
+    m = __builtin_fmaxf(m, unordered_f32(a.part[part_offset(g, rb, N, a.nb, ROWS) + k - rb * ROWS]));
+  a.colmax[q] = m;
+  if (!(m > -__builtin_inff())) return;
+  for (int64_t rb = 0; rb <= rbk; ++rb) {
+    const float p = unordered_f32(a.part[part_offset(g, rb, N, a.nb, ROWS) + k - rb * ROWS]);
+    if (p > -__builtin_inff() && p >= m - kMargin)
+      atomicOr(&a.cbits[((size_t)g * a.nb + rb) * a.words + (k >> 5)], 1u << (k & 31));
+  }
+}
+
+// Exact best twin of the marked positions over one row block: the block's
+// rows are staged in LDS as MFMA A operands (columns of the product), the
+// marked positions gathered as B operands, 32 per wave and round; each lane
+// keeps its half-row maximum and first tile, and the exact fixup of the
+// sweep resolves it.  Pairs with |i - k| <= w and rows past the end are
+// excluded (a pair already seen from the row side changes no maximum).
+template <class S>
+__global__ __launch_bounds__(256) void tri_colres_kernel(TriArgs a) {
+  constexpr int D = S::D;
+  constexpr int ROWS = S::ROWS;
+  constexpr int NT = 256;
+  constexpr int CH = D / 8;
+  constexpr int KS = D / 16;
+  constexpr int LOADS = ROWS * CH / NT;
+  constexpr int TILES = ROWS / 32;
+  constexpr int QCAP = NT * 32;  // keys of one chunk of NT candidate words
+  static_assert(LOADS * NT == ROWS * CH, "block load split");
+  __shared__ StageK<D, ROWS> blk;
+  __shared__ int32_t queue[QCAP];
+  __shared__ int32_t wsum[NT / 64];
+
+  const int64_t N = a.N;
+  const int64_t g = blockIdx.x / a.nb;
+  const int64_t rb = blockIdx.x % a.nb;
+  const int base = (int)(rb * ROWS);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int lrow = lane & 31;
+  const int w = a.window;
+  const uint4* Kg = reinterpret_cast<const uint4*>(a.keys) + (size_t)g * N * CH;
+  const float* rinv_g = a.rinv + (size_t)g * N;
+  const double* nsq_g = a.nsq + (size_t)g * N;
+  const uint32_t* bits = a.cbits + ((size_t)g * a.nb + rb) * a.words;
+  const int nrows = (int)N - base < ROWS ? (int)N - base : ROWS;  // rows of this block
+
+  // stage the block's rows (past the end: the last row) with the sweep's swizzle
+#pragma unroll
+  for (int u = 0; u < LOADS; ++u) {
+    const int qd = tid + NT * u;
+    const int c = qd / CH;
+    const int src = base + (c < nrows ? c : nrows - 1);
+    const int slot = c * CH + ((qd % CH) ^ swz<CH>(c));
+    blk.keys[slot] = Kg[(size_t)src * CH + qd % CH];
+  }
+  for (int c = tid; c < ROWS; c += NT) blk.rinv[c] = rinv_g[base + (c < nrows ? c : nrows - 1)];
+  __syncthreads();
+
+  uint32_t a_off[2][KS];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int cp = 32 * p + lrow;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) a_off[p][s] = (uint32_t)((cp * CH + ((2 * s + h) ^ swz<CH>(cp))) * 16 - p * 32 * CH * 16);
+  }
+
+  const int64_t w0 = base >> 5;  // base is a multiple of 32
+#pragma unroll 1
+  for (int64_t c0 = w0; c0 < a.words; c0 += NT) {
+    // expand this chunk's candidate bits into a position queue
+    const int64_t wi = c0 + tid;
+    const uint32_t word = wi < a.words ? bits[wi] : 0u;
+    int cntw = __popc(word);
+    int incl = cntw;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0, qn = 0;
+#pragma unroll
+    for (int wv = 0; wv < NT / 64; ++wv) {
+      before += wv < wave ? wsum[wv] : 0;
+      qn += wsum[wv];
+    }
+    int pos = before + incl - cntw;
+    uint32_t wb = word;
+    while (wb != 0u) {
+      const int bt = __builtin_ctz(wb);
+      wb &= wb - 1u;
+      queue[pos++] = (int32_t)(wi * 32 + bt);
+    }
+    __syncthreads();
+
+    // rounds of 32 positions per wave
+#pragma unroll 1
+    for (int q0 = 0; q0 < qn; q0 += 4 * 32) {
+      const int qi = q0 + wave * 32 + lrow;
+      const bool ok = qi < qn;
+      const int k = ok ? queue[qi] : queue[q0];  // a lane without a position repeats one (its result is dropped)
+      bf16x8 bk[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) bk[s] = __builtin_bit_cast(bf16x8, Kg[(size_t)k * CH + 2 * s + h]);
+      float bestv = -__builtin_inff();
+      int btile = -1;
+#pragma unroll 1
+      for (int tt = 0; tt < TILES; ++tt) {
+        bf16x8 A[KS];
+        const char* kb = reinterpret_cast<const char*>(blk.keys) + tt * 32 * CH * 16;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + ((tt & 1) ? a_off[1][s] : a_off[0][s])));
+        f32x16 acc = (f32x16){};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], bk[s], acc, 0, 0, 0);
+        float yy[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = tt * 32 + tile_col(r, h);
+          const int i = base + c;
+          const int dist = i > k ? i - k : k - i;
+          yy[r] = (c < nrows && dist > w) ? acc[r] * blk.rinv[c] : -__builtin_inff();
+        }
+        const float m = max16(yy);
+        btile = m > bestv ? tt : btile;
+        bestv = __builtin_fmaxf(bestv, m);
+      }
+      // exact fixup of this block's best, as in the sweep
+      double bb = -1.0;
+      int aa = -1;
+      const double nk = nsq_g[k];
+      const float margin = 8e-5f * (float)sqrt(nk) + 1e-30f;
+      const float other = __shfl_xor(bestv, 32);
+      const bool look = ok && btile >= 0 && bestv >= other - margin;
+      const bool look_o = __shfl_xor((int)look, 32) != 0;
+      const int tile_o = __shfl_xor(btile, 32);
+      const bool look0 = (h == 0) ? look : look_o;
+      const bool look1 = (h == 1) ? look : look_o;
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps) {
+        const int p = (ps == 0 && look0) ? 0 : 1;
+        const bool lk = ps == 0 ? (look0 || look1) : (look0 && look1);
+        const int tp = (h == p) ? btile : tile_o;
+        if (__ballot(lk) == 0ull) continue;
+        if (lk)
+          exact_tile<D>(Kg, nsq_g, rinv_g, k, nk, tp, p, nrows, w, h, margin, [base](int c) { return base + c; }, bb,
+                        aa);
+      }
+      if (h == 0 && ok && aa >= 0) atomicMax((unsigned long long*)&a.best64[(size_t)g * N + k], (unsigned long long)pack_best(bb, aa));
+    }
+    __syncthreads();  // the queue is refilled by the next chunk
+  }
+}
+
+// ---------------------------------------------------------------------------
+// outputs: the exact cosine of the winning pair, counts, scores
+
+template <int D>
+__global__ __launch_bounds__(256) void tri_finalize_kernel(TriArgs a) {
+  constexpr int CH = D / 8;
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= a.G * a.N) return;
+  const int64_t N = a.N;
+  const int64_t g = q / N;
+  const uint64_t u = a.best64[q];
+  double bb = -1.0;
+  int aa = -1;
+  if (u != 0ull) {
+    aa = (int)(kIdxMask - (u & kIdxMask));
+    const uint4* ki = reinterpret_cast<const uint4*>(a.keys) + (size_t)q * CH;
+    const uint4* kj = reinterpret_cast<const uint4*>(a.keys) + ((size_t)g * N + aa) * CH;
+    double dot = 0.0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) dot += dot8_exact(ki[c], kj[c]);
+    const double nn = a.nsq[q] * a.nsq[(size_t)g * N + aa];
+    bb = (nn > 0.0 ? dot / sqrt(nn) : 0.0) + 0.0;
+  }
+  const int c = a.rcount[q] + a.ccount[q];
+  a.best_sim[q] = bb;
+  a.best_idx[q] = aa;
+  a.count[q] = c;
+  const double disc = log((double)(N + 1) / (double)(c + 1));
+  a.score[q] = a.energy[q] * disc;
+  if (a.omega) a.omega[q] = disc / log((double)(N + 1));
+}
+
+__global__ __launch_bounds__(256) void tri_clear_kernel(int32_t* ccount, int64_t n, uint32_t* cbits, int64_t nbits) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n; q += stride) ccount[q] = 0;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < nbits; q += stride) cbits[q] = 0u;
+}
+
+template <class S>
+hipError_t launch_d(const TriArgs& a, hipStream_t stream, hipEvent_t mark) {
+  const int64_t n = a.G * a.N;
+  const int64_t nbits = a.G * a.nb * a.words;
+  int64_t cb = (n > nbits ? n : nbits) / 256 + 1;
+  cb = cb < 8192 ? cb : 8192;
+  hipLaunchKernelGGL(tri_clear_kernel, dim3((unsigned)cb), dim3(256), 0, stream, a.ccount, n, a.cbits, nbits);
+  const int64_t total = a.G * ((a.nb + 1) / 2);
+  const int64_t grid = 8 * ((total + 7) / 8);
+  if (grid > INT_MAX || a.G * a.nb > INT_MAX || (n + 255) / 256 > INT_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((tri_sweep_kernel<S>), dim3((unsigned)grid), dim3(64 * S::WAVES), 0, stream, a);
+  if (mark && hipEventRecord(mark, stream) != hipSuccess) return hipErrorInvalidValue;
+  const unsigned kb = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL((tri_colmax_kernel<S::ROWS>), dim3(kb), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((tri_colres_kernel<S>), dim3((unsigned)(a.G * a.nb)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((tri_finalize_kernel<S::D>), dim3(kb), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int tri_rows(int d) { return d == 64 ? TriShape64::ROWS : TriShape128::ROWS; }
+
+int64_t tri_part_per_head(int64_t N, int rows) {
+  const int64_t nb = (N + rows - 1) / rows;
+  return nb * N - (int64_t)rows * nb * (nb - 1) / 2;
+}
+
+hipError_t launch_tri(const TriArgs& a, hipStream_t stream, hipEvent_t mark) {
+  if (a.d == 64) return launch_d<TriShape64>(a, stream, mark);
+  return launch_d<TriShape128>(a, stream, mark);
+}
+
+}  // namespace twinkv

@@ -15,13 +15,13 @@ workloads).
   its exact cosine (relative to ||k_i||: at most d fp32 roundings of sums of
   exact bf16 products, one of 1/||k_j|| and one of the product, about
   8e-6 at d = 128).  Two candidates less than twice that apart may swap
-  order, so rows whose two best eligible oracle similarities differ by
-  0 < s1 - s2 < NEAR_TIE = 2e-5 may legitimately pick either.  Such a row is
+  order, so a row with an eligible similarity strictly below its maximum by
+  less than NEAR_TIE = 2e-5 may legitimately pick that position.  Such a row is
   not skipped: when the GPU's position differs from the oracle's, the test
   checks that it is an eligible position whose exact cosine lies within
-  NEAR_TIE of the oracle's maximum, and that the GPU reports that cosine.
-  Exact ties (s1 == s2) are not near-ties and must resolve to the lowest
-  position.
+  NEAR_TIE of (and strictly below) the oracle's maximum, and that the GPU
+  reports that cosine.  Exact ties with the maximum must resolve to the
+  lowest position.
 * selection: heads with a band-affected row, or whose kept/evicted boundary
   ranks differ by a relative score gap below 1e-12, are checked by the
   properties a top-k selection must have instead of bit for bit (the oracle
@@ -113,10 +113,14 @@ def _exclusion_stats(K, n, rows, cols, tau, window):
             band[s:s + step] = inb.sum(1)
             c_lo[s:s + step] = (ok & (sims > tau) & ~inb).sum(1)
         if cols.size >= 2:
+            # gap to the largest eligible similarity strictly below the
+            # maximum (exact ties do not make a near-tie: they must resolve
+            # to the lowest position)
             masked = np.where(ok, sims, -np.inf)
-            top = np.partition(masked, -2, axis=1)[:, -2:]
+            best = masked.max(1)
+            below = np.where(masked < best[:, None], masked, -np.inf).max(1)
             with np.errstate(invalid="ignore"):
-                gap[s:s + step] = np.where(np.isfinite(top[:, 0]), top[:, 1] - top[:, 0], np.inf)
+                gap[s:s + step] = np.where(np.isfinite(below) & np.isfinite(best), best - below, np.inf)
     return band, c_lo, gap
 
 
@@ -140,6 +144,8 @@ def validate_near_tie_picks(ref, rows, ga, gb, allowed=None, tag=""):
             assert allowed[j] != 0, f"{tag} row {i}: near-tie pick {j} is not retained"
         sim = float(O.cosine_rows(K, n, np.array([i]), np.array([j]))[0, 0])
         assert sim >= ref["best"][t] - NEAR_TIE, f"{tag} row {i}: pick {j} at {sim} vs max {ref['best'][t]}"
+        # an exact tie with the maximum must go to the lowest position, the oracle's
+        assert sim < ref["best"][t], f"{tag} row {i}: pick {j} ties the maximum but is not the lowest position"
         assert abs(gb[t] - sim) <= EXACT_SIM_RTOL * abs(sim), f"{tag} row {i}: reported {gb[t]} for {sim}"
     return int(diff.sum())
 

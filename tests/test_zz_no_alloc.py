@@ -35,6 +35,8 @@ def test_score_noalloc_matches_score_on_two_calls():
         torch.cuda.synchronize()
         for k in KEYS:
             assert torch.equal(got[k], ref[k]), f"workload {cfg_id} G={G} N={N}: {k} differs"
+        p = krs.params(G, N, cfg.d, cfg.tau, cfg.window)
+        assert krs.workspace_bytes(L.OP_SCORE, p) <= L.NOALLOC_SCRATCH_BYTES
         print(f"[noalloc] G={G} N={N}: all outputs bit-equal, twins {int((got['count'] > 0).sum())}", flush=True)
 
 
@@ -42,8 +44,9 @@ def test_score_noalloc_refuses_sizes_beyond_the_scratch():
     lib = krs.load()
     fake = torch.empty(16, dtype=torch.float64, device="cuda:0")
     ptr = L._ptr(fake)
-    for G, N in ((1, L.NOALLOC_MAX_KEYS + 1), (3, L.NOALLOC_MAX_KEYS // 2)):
-        p = krs.params(G, N, 64, 0.9, 8)
+    for G, N, d in ((1, 1 << 21, 64), (64, 32768, 64), (32, 32768, 128)):
+        p = krs.params(G, N, d, 0.9, 8)
+        assert krs.workspace_bytes(L.OP_SCORE, p) > L.NOALLOC_SCRATCH_BYTES
         st = lib.twinkv_score_noalloc(__import__("ctypes").byref(p), ptr, ptr, ptr, ptr, ptr, ptr, ptr, None, None,
                                       None)
         assert st == L.ERR_TOO_LARGE, st
