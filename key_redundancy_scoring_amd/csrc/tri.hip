@@ -337,18 +337,19 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
       for (int tt = 0; tt < TILES; ++tt) bits |= (unsigned)(col_start + (st * TILES + tt) * 32 + 31 >= (int)N) << tt;
       return bits;
     };
-    // counts of y > tau*||k_i|| over the 16 values of block b: the row's, and
-    // (atomically, rare) each column's; (y > thr read off the sign of thr - y)
-    auto count16 = [&](const f32x16& y, int b) TWINKV_INLINE {
-      uint32_t c = 0;
+    // counts of y > tau*||k_i|| over the 16 values of block b (y > thr read
+    // off the sign of thr - y): the row's, and, one atomic per twin, each
+    // column's
+    auto count16 = [&](const f32x16& y, int b, int c0) TWINKV_INLINE {
+      uint32_t msk = 0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) c += __float_as_uint(thr[b] - y[r]) >> 31;
-      cnt[b] += (int)c;
-    };
-    auto colcount16 = [&](const f32x16& y, int b, int c0) TWINKV_INLINE {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (__float_as_uint(thr[b] - y[r]) >> 31) atomicAdd(&ccount_g[c0 + tile_col(r, h)], 1);
+      for (int r = 0; r < 16; ++r) msk |= (__float_as_uint(thr[b] - y[r]) >> 31) << r;
+      cnt[b] += __popc(msk);
+      while (msk != 0u) {
+        const int r = __builtin_ctz(msk);
+        msk &= msk - 1u;
+        atomicAdd(&ccount_g[c0 + tile_col(r, h)], 1);
+      }
     };
     auto mfma_block = [&](const bf16x8 (&A)[KS], int b, f32x16& acc) TWINKV_INLINE {
       acc = (f32x16){};
@@ -375,10 +376,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
       if (live) {  // wave-uniform
         btile[b] = m > best[b] ? tile : btile[b];
         best[b] = __builtin_fmaxf(best[b], m);
-        if (__ballot(m > thr[b]) != 0ull) {
-          count16(acc, b);
-          colcount16(acc, b, c0);
-        }
+        if (__ballot(m > thr[b]) != 0ull) count16(acc, b, c0);
       }
     };
     const int slot = slot_of_lane(lane);
@@ -581,38 +579,70 @@ __global__ __launch_bounds__(256) void tri_colmax_kernel(TriArgs a) {
   const int64_t N = a.N;
   const int64_t g = q / N;
   const int64_t k = q % N;
-  const int64_t rbk = k / ROWS;  // row blocks 0..rbk swept column k
-  float m = a.rowcos[q];
-  for (int64_t rb = 0; rb <= rbk; ++rb)
-    m = __builtin_fmaxf(m, unordered_f32(a.part[part_offset(g, rb, N, a.nb, ROWS) + k - rb * ROWS]));
+  const int rbk = (int)(k / ROWS);  // row blocks 0..rbk swept column k
+  // column k of block rb sits at part_offset(g, rb) + k - rb*ROWS; the next
+  // block's entry is N - (rb+1)*ROWS further on
+  const int32_t* p0 = a.part + part_offset(g, 0, N, a.nb, ROWS) + k;
+  float p1 = -__builtin_inff(), p2 = -__builtin_inff();
+  int r1 = -1;
+  {
+    const int32_t* pp = p0;
+#pragma unroll 4
+    for (int rb = 0; rb <= rbk; ++rb) {
+      const float p = unordered_f32(*pp);
+      pp += N - (int64_t)(rb + 1) * ROWS;
+      const bool top = p > p1;
+      p2 = top ? p1 : __builtin_fmaxf(p2, p);
+      r1 = top ? rb : r1;
+      p1 = top ? p : p1;
+    }
+  }
+  const float m = __builtin_fmaxf(a.rowcos[q], p1);
   a.colmax[q] = m;
-  if (!(m > -__builtin_inff())) return;
-  for (int64_t rb = 0; rb <= rbk; ++rb) {
-    const float p = unordered_f32(a.part[part_offset(g, rb, N, a.nb, ROWS) + k - rb * ROWS]);
-    if (p > -__builtin_inff() && p >= m - kMargin)
-      atomicOr(&a.cbits[((size_t)g * a.nb + rb) * a.words + (k >> 5)], 1u << (k & 31));
+  if (!(p1 > -__builtin_inff()) || p1 < m - kMargin) return;
+  uint32_t* bits = a.cbits + (size_t)g * a.nb * a.words + (k >> 5);
+  const uint32_t bit = 1u << (k & 31);
+  if (!(p2 >= m - kMargin)) {  // the usual case: one block within the margin
+    atomicOr(bits + (size_t)r1 * a.words, bit);
+    return;
+  }
+  const int32_t* pp = p0;
+  for (int rb = 0; rb <= rbk; ++rb) {
+    const float p = unordered_f32(*pp);
+    pp += N - (int64_t)(rb + 1) * ROWS;
+    if (p > -__builtin_inff() && p >= m - kMargin) atomicOr(bits + (size_t)rb * a.words, bit);
   }
 }
 
-// Exact best twin of the marked positions over one row block: the block's
-// rows are staged in LDS as MFMA A operands (columns of the product), the
-// marked positions gathered as B operands, 32 per wave and round; each lane
-// keeps its half-row maximum and first tile, and the exact fixup of the
-// sweep resolves it.  Pairs with |i - k| <= w and rows past the end are
-// excluded (a pair already seen from the row side changes no maximum).
+// Exact best twin of the marked positions over one row block.  The block's
+// rows are staged in LDS as MFMA A operands (with their squared and inverse
+// norms); the marked positions are gathered as B operands, 32 per wave and
+// round, rounds kept full by queueing the positions of several candidate
+// words.  A row is a candidate when its fp32 value reaches the position's
+// overall maximum minus the margin: usually one row per position, the one
+// that attains the maximum.  Each half-row lane notes its first candidate;
+// afterwards the candidates are recomputed exactly in fp64 from the staged
+// row and the position's own chunks (the two lanes that hold a position add
+// their halves), and a position with more than one candidate in a half has
+// its tiles swept again with every candidate recomputed.  The best goes to
+// the 64-bit atomic maximum.  Pairs with |i - k| <= w and rows past the end
+// are excluded (a pair also on k's row side changes no maximum).
 template <class S>
-__global__ __launch_bounds__(256) void tri_colres_kernel(TriArgs a) {
+__global__ __launch_bounds__(256, S::D == 64 ? 2 : 1) void tri_colres_kernel(TriArgs a) {
   constexpr int D = S::D;
   constexpr int ROWS = S::ROWS;
   constexpr int NT = 256;
   constexpr int CH = D / 8;
   constexpr int KS = D / 16;
-  constexpr int LOADS = ROWS * CH / NT;
   constexpr int TILES = ROWS / 32;
-  constexpr int QCAP = NT * 32;  // keys of one chunk of NT candidate words
-  static_assert(LOADS * NT == ROWS * CH, "block load split");
+  constexpr int WCHUNK = NT / 2;              // candidate words expanded at a time (by the first half)
+  constexpr int ROUND = 4 * 32;               // positions per round
+  constexpr int QCAP = WCHUNK * 32 + ROUND;   // a chunk's positions plus a partial round carried over
+  static_assert((ROWS * CH) % NT == 0, "block load split");
   __shared__ StageK<D, ROWS> blk;
+  __shared__ double bnsq[ROWS];
   __shared__ int32_t queue[QCAP];
+  __shared__ int32_t qcount;
   __shared__ int32_t wsum[NT / 64];
 
   const int64_t N = a.N;
@@ -626,21 +656,29 @@ __global__ __launch_bounds__(256) void tri_colres_kernel(TriArgs a) {
   const int lrow = lane & 31;
   const int w = a.window;
   const uint4* Kg = reinterpret_cast<const uint4*>(a.keys) + (size_t)g * N * CH;
-  const float* rinv_g = a.rinv + (size_t)g * N;
-  const double* nsq_g = a.nsq + (size_t)g * N;
   const uint32_t* bits = a.cbits + ((size_t)g * a.nb + rb) * a.words;
   const int nrows = (int)N - base < ROWS ? (int)N - base : ROWS;  // rows of this block
 
-  // stage the block's rows (past the end: the last row) with the sweep's swizzle
+  // the block's rows (past the end: the last row) straight into LDS with the
+  // sweep's swizzle: slot s = c*CH + (chunk ^ swz(c)) is written by the lane
+  // that fetches that chunk of row c
+  {
+    constexpr int LD = ROWS * CH / NT;
 #pragma unroll
-  for (int u = 0; u < LOADS; ++u) {
-    const int qd = tid + NT * u;
-    const int c = qd / CH;
-    const int src = base + (c < nrows ? c : nrows - 1);
-    const int slot = c * CH + ((qd % CH) ^ swz<CH>(c));
-    blk.keys[slot] = Kg[(size_t)src * CH + qd % CH];
+    for (int u = 0; u < LD; ++u) {
+      const int sl = NT * u + tid;
+      const int c = sl / CH;
+      const int chunk = (sl % CH) ^ swz<CH>(c);
+      dma16(Kg + (size_t)(base + (c < nrows ? c : nrows - 1)) * CH + chunk, &blk.keys[NT * u + wave * 64]);
+    }
+    for (int c = tid; c < ROWS; c += NT) {
+      const int src = base + (c < nrows ? c : nrows - 1);
+      blk.rinv[c] = a.rinv[(size_t)g * N + src];
+      bnsq[c] = a.nsq[(size_t)g * N + src];
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
   }
-  for (int c = tid; c < ROWS; c += NT) blk.rinv[c] = rinv_g[base + (c < nrows ? c : nrows - 1)];
+  if (tid == 0) qcount = 0;
   __syncthreads();
 
   uint32_t a_off[2][KS];
@@ -651,14 +689,128 @@ __global__ __launch_bounds__(256) void tri_colres_kernel(TriArgs a) {
     for (int s = 0; s < KS; ++s) a_off[p][s] = (uint32_t)((cp * CH + ((2 * s + h) ^ swz<CH>(cp))) * 16 - p * 32 * CH * 16);
   }
 
-  const int64_t w0 = base >> 5;  // base is a multiple of 32
+  // exact cosine of position k (chunks kc of this lane's half) with staged row
+  // c; both lanes of the position call it together
+  auto exact = [&](const uint4 (&kc)[KS], double nk, int c) TWINKV_INLINE {
+    double part = 0.0;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) part += dot8_exact(kc[s], blk.keys[c * CH + ((2 * s + h) ^ swz<CH>(c))]);
+    const double dot = part + __shfl_xor(part, 32);
+    const double nn = nk * bnsq[c];
+    const double sim = nn > 0.0 ? dot / sqrt(nn) : 0.0;
+    return sim + 0.0;
+  };
+  auto tile_dots = [&](int tt, const bf16x8 (&bk)[KS]) TWINKV_INLINE {
+    bf16x8 A[KS];
+    const char* kb = reinterpret_cast<const char*>(blk.keys) + tt * 32 * CH * 16;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + ((tt & 1) ? a_off[1][s] : a_off[0][s])));
+    f32x16 acc = (f32x16){};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], bk[s], acc, 0, 0, 0);
+    return acc;
+  };
+  // candidate rows of a tile: y = dot/||k_row|| >= thr; the window and the
+  // end of the block are tested only on tiles that reach them
+  auto cand_mask = [&](const f32x16& acc, int tt, int k, float thr) TWINKV_INLINE {
+    float rv[16];
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const float4 r4 = *reinterpret_cast<const float4*>(&blk.rinv[tt * 32 + 8 * gq + 4 * h]);
+      rv[4 * gq + 0] = r4.x;
+      rv[4 * gq + 1] = r4.y;
+      rv[4 * gq + 2] = r4.z;
+      rv[4 * gq + 3] = r4.w;
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m |= (uint32_t)(acc[r] * rv[r] >= thr) << r;
+    const int lo = base + tt * 32;  // rows lo .. lo + 31
+    const bool edge = lo + 31 >= k - w && lo <= k + w;
+    if (__ballot(edge || tt * 32 + 31 >= nrows) != 0ull) {
+      uint32_t keep = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = tt * 32 + tile_col(r, h);
+        const int i = base + c;
+        const int dist = i > k ? i - k : k - i;
+        keep |= (uint32_t)(c < nrows && dist > w) << r;
+      }
+      m &= keep;
+    }
+    return m;
+  };
+  auto process = [&](int q0, int qn) TWINKV_INLINE {
+    const int qi = q0 + wave * 32 + lrow;
+    const bool ok = qi < qn;
+    const int k = queue[ok ? qi : q0];  // a lane without a position repeats one; its result is dropped
+    uint4 kc[KS];
+    bf16x8 bk[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      kc[s] = Kg[(size_t)k * CH + 2 * s + h];
+      bk[s] = __builtin_bit_cast(bf16x8, kc[s]);
+    }
+    const double nk = a.nsq[(size_t)g * N + k];
+    // y = dot/||k_row|| = ||k|| cos: rows within the margin of k's overall maximum
+    const float thr = ok ? (a.colmax[(size_t)g * N + k] - kMargin) * (float)sqrt(nk) : __builtin_inff();
+    int first = -1;  // this half's first candidate (staged row), -2: more than one
 #pragma unroll 1
-  for (int64_t c0 = w0; c0 < a.words; c0 += NT) {
-    // expand this chunk's candidate bits into a position queue
+    for (int tt = 0; tt < TILES; ++tt) {
+      const f32x16 acc = tile_dots(tt, bk);
+      const uint32_t m = cand_mask(acc, tt, k, thr);
+      if (m != 0u) first = (first == -1 && (m & (m - 1u)) == 0u) ? tt * 32 + tile_col(__builtin_ctz(m), h) : -2;
+    }
+    double bb = -1.0;
+    int aa = -1;
+    auto take = [&](double sim, int c) TWINKV_INLINE {
+      const int j = base + c;
+      if (aa < 0 || sim > bb || (sim == bb && j < aa)) {
+        bb = sim;
+        aa = j;
+      }
+    };
+    const int other = __shfl_xor(first, 32);
+    // the single candidates of half 0, then half 1
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int c = (h == p) ? first : other;
+      if (__ballot(c >= 0) == 0ull) continue;
+      if (c >= 0) take(exact(kc, nk, c), c);
+    }
+    // positions with several candidates in a half: every candidate, exactly
+    if (__ballot(first == -2 || other == -2) != 0ull) {
+      const bool redo = first == -2 || other == -2;
+#pragma unroll 1
+      for (int tt = 0; tt < TILES; ++tt) {
+        const f32x16 acc = tile_dots(tt, bk);
+        const uint32_t mine = redo ? cand_mask(acc, tt, k, thr) : 0u;
+        const uint32_t oth = (uint32_t)__shfl_xor((int)mine, 32);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          uint32_t cm = (h == p) ? mine : oth;
+          while (cm != 0u) {
+            const int r = __builtin_ctz(cm);
+            cm &= cm - 1u;
+            const int c = tt * 32 + tile_col(r, p);
+            take(exact(kc, nk, c), c);
+          }
+        }
+      }
+    }
+    if (h == 0 && ok && aa >= 0)
+      atomicMax((unsigned long long*)&a.best64[(size_t)g * N + k], (unsigned long long)pack_best(bb, aa));
+  };
+
+#pragma unroll 1
+  for (int64_t c0 = base >> 5; c0 < a.words; c0 += WCHUNK) {  // base is a multiple of 32
+    // each of the first WCHUNK threads expands one word; a workgroup scan
+    // places its positions
     const int64_t wi = c0 + tid;
-    const uint32_t word = wi < a.words ? bits[wi] : 0u;
-    int cntw = __popc(word);
-    int incl = cntw;
+    const uint32_t word = (tid < WCHUNK && wi < a.words) ? bits[wi] : 0u;
+    const int cw = __popc(word);
+    int incl = cw;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int v = __shfl_up(incl, off);
@@ -666,13 +818,14 @@ __global__ __launch_bounds__(256) void tri_colres_kernel(TriArgs a) {
     }
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
-    int before = 0, qn = 0;
+    const int q = qcount;  // fewer than ROUND carried over
+    int before = 0, total = 0;
 #pragma unroll
     for (int wv = 0; wv < NT / 64; ++wv) {
       before += wv < wave ? wsum[wv] : 0;
-      qn += wsum[wv];
+      total += wsum[wv];
     }
-    int pos = before + incl - cntw;
+    int pos = q + before + incl - cw;
     uint32_t wb = word;
     while (wb != 0u) {
       const int bt = __builtin_ctz(wb);
@@ -680,64 +833,21 @@ __global__ __launch_bounds__(256) void tri_colres_kernel(TriArgs a) {
       queue[pos++] = (int32_t)(wi * 32 + bt);
     }
     __syncthreads();
-
-    // rounds of 32 positions per wave
+    const int qn = q + total;
+    const bool last = c0 + WCHUNK >= a.words;
+    const int full = last ? qn : qn - qn % ROUND;  // whole rounds now, the rest with the next chunk
 #pragma unroll 1
-    for (int q0 = 0; q0 < qn; q0 += 4 * 32) {
-      const int qi = q0 + wave * 32 + lrow;
-      const bool ok = qi < qn;
-      const int k = ok ? queue[qi] : queue[q0];  // a lane without a position repeats one (its result is dropped)
-      bf16x8 bk[KS];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) bk[s] = __builtin_bit_cast(bf16x8, Kg[(size_t)k * CH + 2 * s + h]);
-      float bestv = -__builtin_inff();
-      int btile = -1;
-#pragma unroll 1
-      for (int tt = 0; tt < TILES; ++tt) {
-        bf16x8 A[KS];
-        const char* kb = reinterpret_cast<const char*>(blk.keys) + tt * 32 * CH * 16;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + ((tt & 1) ? a_off[1][s] : a_off[0][s])));
-        f32x16 acc = (f32x16){};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], bk[s], acc, 0, 0, 0);
-        float yy[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = tt * 32 + tile_col(r, h);
-          const int i = base + c;
-          const int dist = i > k ? i - k : k - i;
-          yy[r] = (c < nrows && dist > w) ? acc[r] * blk.rinv[c] : -__builtin_inff();
-        }
-        const float m = max16(yy);
-        btile = m > bestv ? tt : btile;
-        bestv = __builtin_fmaxf(bestv, m);
-      }
-      // exact fixup of this block's best, as in the sweep
-      double bb = -1.0;
-      int aa = -1;
-      const double nk = nsq_g[k];
-      const float margin = 8e-5f * (float)sqrt(nk) + 1e-30f;
-      const float other = __shfl_xor(bestv, 32);
-      const bool look = ok && btile >= 0 && bestv >= other - margin;
-      const bool look_o = __shfl_xor((int)look, 32) != 0;
-      const int tile_o = __shfl_xor(btile, 32);
-      const bool look0 = (h == 0) ? look : look_o;
-      const bool look1 = (h == 1) ? look : look_o;
-#pragma unroll
-      for (int ps = 0; ps < 2; ++ps) {
-        const int p = (ps == 0 && look0) ? 0 : 1;
-        const bool lk = ps == 0 ? (look0 || look1) : (look0 && look1);
-        const int tp = (h == p) ? btile : tile_o;
-        if (__ballot(lk) == 0ull) continue;
-        if (lk)
-          exact_tile<D>(Kg, nsq_g, rinv_g, k, nk, tp, p, nrows, w, h, margin, [base](int c) { return base + c; }, bb,
-                        aa);
-      }
-      if (h == 0 && ok && aa >= 0) atomicMax((unsigned long long*)&a.best64[(size_t)g * N + k], (unsigned long long)pack_best(bb, aa));
+    for (int q0 = 0; q0 < full; q0 += ROUND) process(q0, full);
+    __syncthreads();
+    if (!last) {  // carry the partial round to the front
+      const int rest = qn - full;
+      int v = 0;
+      if (tid < rest) v = queue[full + tid];
+      __syncthreads();
+      if (tid < rest) queue[tid] = v;
+      if (tid == 0) qcount = rest;
+      __syncthreads();
     }
-    __syncthreads();  // the queue is refilled by the next chunk
   }
 }
 
