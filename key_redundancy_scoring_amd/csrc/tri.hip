@@ -320,23 +320,6 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
     // first and last row position of the wave (rows past the end clamped)
     const int rlo = __builtin_amdgcn_readfirstlane(row0 < N ? row0 : (int)N - 1);
     const int rhi = __builtin_amdgcn_readfirstlane(row0 + RB * 32 - 1 < N ? row0 + RB * 32 - 1 : (int)N - 1);
-    // bit tt: tile tt of stage st holds a pair with j - i <= w (or reaches the
-    // end); only tiles wholly past the band of every row of the wave are swept
-    auto masked_tiles = [&](int st) TWINKV_INLINE {
-      unsigned bits = 0;
-#pragma unroll
-      for (int tt = 0; tt < TILES; ++tt) {
-        const int c0 = col_start + (st * TILES + tt) * 32;
-        bits |= (unsigned)((c0 <= rhi + w) || (c0 + 31 >= (int)N)) << tt;
-      }
-      return bits;
-    };
-    auto tail_tiles = [&](int st) TWINKV_INLINE {
-      unsigned bits = 0;
-#pragma unroll
-      for (int tt = 0; tt < TILES; ++tt) bits |= (unsigned)(col_start + (st * TILES + tt) * 32 + 31 >= (int)N) << tt;
-      return bits;
-    };
     // counts of y > tau*||k_i|| over the 16 values of block b (y > thr read
     // off the sign of thr - y): the row's, and, one atomic per twin, each
     // column's
@@ -404,130 +387,144 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
       }
     };
 
-    // ---- the sweep (the rolling pipeline of the two-order sweep)
+    // ---- the sweep.  The stages at the start that hold a pair with j - i <=
+    // w for some row of the workgroup (the diagonal) and a ragged last stage
+    // run tile by tile from LDS, masking pairs with j - i <= w, columns past
+    // the end and rows past the end; the clean stages between them (every tile
+    // past the band of every row) run the rolling pipeline of the two-order
+    // sweep unmasked.  Tiles are visited in column order, so the first tile
+    // attaining a row's maximum is kept.
     const int nstages = (ncols + SC - 1) / SC;
     const int tile0 = col_start >> 5;
+    const int wg_rhi = col_start + ROWS - 1 < N ? col_start + ROWS - 1 : (int)N - 1;
+    // leading stages that reach the band, rounded up to an even count so the
+    // pipelined stages start in the first buffer
+    const int nd0 = ((wg_rhi + w - col_start) / SC + 2) & ~1;
+    const int nd = nd0 < nstages ? nd0 : nstages;
+    const int nce = (ncols % SC == 0) ? nstages : nstages - 1;  // stages before a ragged last one
     f32x16 acc[RB];
     bf16x8 A[KS];
     float rv[16];
-    int band_lo = INT_MAX, band_hi = -1;  // masked tiles other than the tail (absolute tile ids)
-    if (nstages > 0) issue(0, buf0);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-    if (nstages > 1) issue(SC, buf1);
-    if (nstages > 0) {
-      load_a(buf0, 0, 0, A);
+
+    // one tile's epilogue with every pair tested
+    auto masked_epilogue = [&](f32x16& accb, int b, int tile, int c0) TWINKV_INLINE {
+      const int i = row0 + 32 * b + lrow;
+      float yy[16];
+      int twins = 0;
 #pragma unroll
-      for (int b = 0; b < RB; ++b) mfma_block(A, b, acc[b]);
-      load_rv(buf0, 0, rv);
-    }
-    auto stage = [&](int st, StageK<D, SC>& cur, const StageK<D, SC>& nxt) TWINKV_INLINE {
-      const unsigned mbits = __builtin_amdgcn_readfirstlane(masked_tiles(st));
-      const unsigned bbits = mbits & ~__builtin_amdgcn_readfirstlane(tail_tiles(st));
-      if (bbits != 0u) {
-        band_lo = min(band_lo, tile0 + st * TILES + __builtin_ctz(bbits));
-        band_hi = max(band_hi, tile0 + st * TILES + 31 - __builtin_clz(bbits));
+      for (int r = 0; r < 16; ++r) {
+        const int col = c0 + tile_col(r, h);
+        const bool ok = i < N && col < N && col - i > w;
+        yy[r] = ok ? accb[r] * rv[r] : -__builtin_inff();
+        const float z = ok ? yy[r] * rinvr[b] : -__builtin_inff();
+        colmax[r] = (b == 0) ? z : __builtin_fmaxf(colmax[r], z);
+        const bool tw = ok && yy[r] > thr[b];
+        twins += tw ? 1 : 0;
+        if (tw) atomicAdd(&ccount_g[col], 1);
       }
+      cnt[b] += twins;
+      const float m = max16(yy);
+      btile[b] = m > best[b] ? tile : btile[b];
+      best[b] = __builtin_fmaxf(best[b], m);
+    };
+    // a stage run tile by tile; its data was issued before (into the buffer
+    // of its parity)
+    auto masked_stage = [&](int st) TWINKV_INLINE {
+      StageK<D, SC>& cur = (st & 1) ? buf1 : buf0;
+      StageK<D, SC>& nxt = (st & 1) ? buf0 : buf1;
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      if (st >= 1) merge_stage(st - 1);
+      if (st + 1 < nstages) issue((st + 1) * SC, nxt);
+#pragma unroll 1
+      for (int tt = 0; tt < TILES; ++tt) {
+        const int tile = tile0 + st * TILES + tt;
+        const int c0 = tile * 32;
+        if (c0 >= N) break;  // past the end (wave-uniform); these columns are never merged
+        if (c0 + 31 <= rlo + w) {  // no pair of this tile has j - i > w for this wave
+          if ((lane & 1) == 0) colpart[st % 3][wave][tt * 32 + tile_col(slot, h)] = -__builtin_inff();
+          continue;
+        }
+        const bool live = c0 > rhi + w && c0 + 31 < N;  // wave-uniform
+        load_a(cur, tt, tt & 1, A);
+        load_rv(cur, tt, rv);
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          f32x16 y;
+          mfma_block(A, b, y);
+          if (live) epilogue(y, b, rv, true, tile, c0);
+          else masked_epilogue(y, b, tile, c0);
+        }
+        flush_cols(st, tt, true);
+      }
+    };
+    // the rolling pipeline over a clean stage: after block b's epilogue for
+    // tile t its accumulator takes the MFMAs of tile t+1; the last tile's
+    // epilogue overlaps the next stage's first MFMAs when that stage is clean
+    auto stage = [&](int st, StageK<D, SC>& cur, const StageK<D, SC>& nxt) TWINKV_INLINE {
 #pragma unroll 1
       for (int tt = 0; tt < TILES - 1; ++tt) {
         const int tile = tile0 + st * TILES + tt;
         load_a(cur, tt + 1, (tt + 1) & 1, A);
-        const bool live = ((mbits >> tt) & 1u) == 0u;
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
-          epilogue(acc[b], b, rv, live, tile, tile * 32);
+          epilogue(acc[b], b, rv, true, tile, tile * 32);
           mfma_block(A, b, acc[b]);
           interleave();
         }
-        flush_cols(st, tt, live);
+        flush_cols(st, tt, true);
         load_rv(cur, tt + 1, rv);
       }
-      const bool more = st + 1 < nstages;
+      const bool more = st + 1 < nce;
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
       if (st >= 1) merge_stage(st - 1);
       if (st + 2 < nstages) issue((st + 2) * SC, cur);
       if (more) load_a(nxt, 0, 0, A);
       const int tile = tile0 + st * TILES + TILES - 1;
-      const bool live = ((mbits >> (TILES - 1)) & 1u) == 0u;
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
-        epilogue(acc[b], b, rv, live, tile, tile * 32);
+        epilogue(acc[b], b, rv, true, tile, tile * 32);
         if (more) mfma_block(A, b, acc[b]);
         interleave();
       }
-      flush_cols(st, TILES - 1, live);
+      flush_cols(st, TILES - 1, true);
       if (more) load_rv(nxt, 0, rv);
     };
+
+    // stages [0, nd) and [max(nd, nce), nstages) run masked, tile by tile
+    auto masked_run = [&](int from, int to) TWINKV_INLINE {
 #pragma unroll 1
-    for (int st = 0; st < nstages; st += 2) {
-      stage(st, buf0, buf1);
-      if (st + 1 >= nstages) break;
-      stage(st + 1, buf1, buf0);
+      for (int st = from; st < to; ++st) masked_stage(st);
+    };
+    issue(0, buf0);
+    int st_m = 0, st_end = nd;  // the masked range to run next
+#pragma unroll 1
+    for (int part = 0; part < 2; ++part) {
+      masked_run(st_m, st_end);
+      if (part == 1) break;
+      if (nd < nce) {
+        // stage nd (even: the first buffer) was issued by the last diagonal stage
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __syncthreads();
+        if (nd + 1 < nstages) issue((nd + 1) * SC, buf1);
+        load_a(buf0, 0, 0, A);
+#pragma unroll
+        for (int b = 0; b < RB; ++b) mfma_block(A, b, acc[b]);
+        load_rv(buf0, 0, rv);
+#pragma unroll 1
+        for (int st = nd; st < nce; st += 2) {
+          stage(st, buf0, buf1);
+          if (st + 1 >= nce) break;
+          stage(st + 1, buf1, buf0);
+        }
+      }
+      // then the stages past both: a ragged last stage (or none)
+      st_m = nd > nce ? nd : nce;
+      st_end = nstages;
     }
     __syncthreads();
     if (nstages > 0) merge_stage(nstages - 1);
-    // every plain store of the column maxima is complete before the masked
-    // tiles add theirs atomically
-    __syncthreads();
-
-    // ---- masked tiles (the band range, the partial last tile), from global
-    // memory, with pairs j - i <= w, columns past the end and rows past the
-    // end excluded.  Tiles wholly on or below the band of every row are
-    // skipped.  An exact tie with the running maximum goes to the lower tile.
-    {
-      const int ntiles = tile0 + (ncols + 31) / 32;  // absolute end
-      const int last = ntiles - 1;
-      const int nband = band_hi >= 0 ? band_hi - band_lo + 1 : 0;
-      const bool last_extra = ncols > 0 && (ncols & 31) != 0 && !(nband > 0 && last >= band_lo && last <= band_hi);
-      const int nproc = nband + (last_extra ? 1 : 0);
-#pragma unroll 1
-      for (int k = 0; k < nproc; ++k) {
-        const int t = k < nband ? band_lo + k : last;
-        const int c0 = t * 32;
-        if (c0 + 31 <= rlo + w) continue;  // no pair of this tile has j - i > w (wave-uniform)
-        bf16x8 Am[KS];
-        {
-          const int c = c0 + lrow < N ? c0 + lrow : (int)N - 1;
-#pragma unroll
-          for (int s = 0; s < KS; ++s) Am[s] = __builtin_bit_cast(bf16x8, Kg[(size_t)c * CH + 2 * s + h]);
-        }
-        float rvm[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int col = c0 + tile_col(r, h);
-          rvm[r] = rinv_g[col < N ? col : N - 1];
-        }
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-          f32x16 y;
-          mfma_block(Am, b, y);
-          const int i = row0 + 32 * b + lrow;
-          float yy[16];
-          int twins = 0;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int col = c0 + tile_col(r, h);
-            const bool ok = i < N && col < N && col - i > w;
-            yy[r] = ok ? y[r] * rvm[r] : -__builtin_inff();
-            const float z = ok ? yy[r] * rinvr[b] : -__builtin_inff();
-            colmax[r] = (b == 0) ? z : __builtin_fmaxf(colmax[r], z);
-            const bool tw = ok && yy[r] > thr[b];
-            twins += tw ? 1 : 0;
-            if (tw) atomicAdd(&ccount_g[col], 1);
-          }
-          cnt[b] += twins;
-          const float m = max16(yy);
-          if (m > best[b] || (m == best[b] && t < btile[b])) {
-            best[b] = m;
-            btile[b] = t;
-          }
-        }
-        const float v = reduce_scatter16(colmax);
-        const int col = c0 + tile_col(slot, h);
-        if ((lane & 1) == 0 && col < N && v > -__builtin_inff()) atomicMax(&part_rb[col - col_start], ordered_f32(v));
-      }
-    }
 
     // ---- exact row side: per half-row, the fp32 maximum and its first tile;
     // a half within the margin of the row's maximum is screened and its
