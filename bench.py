@@ -8,8 +8,10 @@ One step = one pass of the workload's whole path over one batch of synthetic
 heads that is already resident in HBM:
 
 * score workloads (tiny, Llama-3.2-1B 32k -- the default --, long 131k,
-  batched 8k): score (norms/energy pass + fused Gram sweep with the fp64
-  best-twin fixup and the discounted score) -> exact-budget select -> repair
+  batched 8k): score (norms/energy pass + single-order Gram sweep that takes
+  each unordered nonlocal pair once, for both its row and its column, then
+  the resolve of column maxima with the fp64 best-twin fixup and the
+  discounted score) -> exact-budget select -> repair
   of the selected set (compaction of the retained keys, restricted Gram over
   them for the rows whose unrestricted twin was evicted, orphan/donor
   ranking and swap);
@@ -18,20 +20,23 @@ heads that is already resident in HBM:
   and no prior: every row is swept against the K = N/2 retained columns.
 
 Prints one JSON line.  `value` is keys (head positions) through the whole
-path per second.  `roofline` is for the dominant kernel (the score-mode Gram
-sweep; the restricted repair sweep in the repair workload), timed with HIP
-events that the library records around its launch on the stream it runs on.
-Its `achieved` counts the algorithmic work: one d-length dot product (2d
-flop) per unordered nonlocal pair in score mode, per (row, retained column)
-pair in repair mode; `gram` also gives the dense-equivalent rate (both orders
-of every pair, the work the score sweep executes).  `traffic` is the HBM
-traffic per launch measured with rocprofv3 counters for the current Gram
-source (null when the source has changed since).  Outside the timed step,
-`gather_kv` times the packed cache of the last step's retained set, and in
-score workloads `variant_score` the keys of the permuted-count variant,
-`count_stats` the per-head count statistics against value-only selection and
-`allocate` the per-head capacities from the attention of the last 32
-synthetic prefix queries of each KV head (8 KV heads per layer).
+path per second.  `roofline` is for the dominant kernel (the single-order
+score sweep; the restricted repair sweep in the repair workload), timed with
+HIP events that the library records around its launch on the stream it runs
+on.  Its `achieved` counts the algorithmic work: one d-length dot product
+(2d flop) per unordered nonlocal pair in score mode, per (row, retained
+column) pair in repair mode; `gram` also gives the rate as if the full N x N
+product had been formed (the work a two-sided sweep would execute).
+`traffic` is the HBM traffic per launch measured with rocprofv3 counters for
+the current kernel source (null when the source has changed since).  The
+score phases are `norms_energy`, `score_sweep` and `score_resolve` (column
+maxima, exact re-evaluation of near-maximum column candidates, fp64
+fixup).  Outside the timed step, `gather_kv` times the packed cache of the
+last step's retained set, and in score workloads `variant_score` the keys of
+the permuted-count variant, `count_stats` the per-head count statistics
+against value-only selection and `allocate` the per-head capacities from the
+attention of the last 32 synthetic prefix queries of each KV head (8 KV
+heads per layer).
 
 `cpu_baseline` runs before the GPU is touched: the fp64 oracle's whole step
 on whole heads (one seeded head per host core, first and last head
@@ -58,24 +63,30 @@ METRIC = "keys scored/sec + Gram TFLOP/s (MFMA % of peak) at N=32k, 1 MI355X"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU (published: 2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0
 PEAK_FP64_TFLOPS = 78.6
-GRAM_SOURCE = os.path.join(ROOT, "key_redundancy_scoring_amd", "csrc", "gram.hip")
-# launch shape of the score-mode sweep per head dim, as the kernel trace names it
-SCORE_SHAPE = {64: "GramShape<64, 4, 4, 256, 2>", 128: "GramShape<128, 2, 4, 128, 2>"}
-REPAIR_SHAPE = {64: "GramShape<64, 2, 4, 128, 3>", 128: "GramShape<128, 2, 4, 128, 2>"}
+# the oracle's whole step costs O(N^2 d) fp64 work per head (15-20 s of one
+# host core at N = 32768); longer heads get no CPU baseline
+CPU_BASELINE_MAX_N = 32768
+SOURCES = {"score": os.path.join(ROOT, "key_redundancy_scoring_amd", "csrc", "tri.hip"),
+           "repair": os.path.join(ROOT, "key_redundancy_scoring_amd", "csrc", "gram.hip")}
+# the dominant kernel of each mode per head dim, as the kernel trace names it
+SCORE_KERNEL = {64: "tri_sweep_kernel<GramShape<64, 3, 4, 256, 2>>",
+                128: "tri_sweep_kernel<GramShape<128, 2, 4, 128, 2>>"}
+REPAIR_KERNEL = {64: "gram_kernel<GramShape<64, 2, 4, 128, 3>, repair>",
+                 128: "gram_kernel<GramShape<128, 2, 4, 128, 2>, repair>"}
 
-# HBM traffic of one score-mode Gram launch on the default workload, from
-# rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the counters'
-# reading for a plain device copy of known size; keyed by the sha256 of the
-# Gram source the counters were taken on.
+# HBM traffic of one launch of the dominant kernel, from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE (KiB per dispatch) scaled by the counters' reading for a plain
+# device copy of known size; keyed by the sha256 of the kernel's source file
+# at the time the counters were taken, so a changed kernel reports null.
 MEASURED_TRAFFIC: dict = {
-    "8e228c205b2f4f0945eb331799a250fe6168612366bc8425fb4467f59077fa47": {
+    "c2747777f9f57c8d476a142f056e2ef4ca511373b94cbf5e737fe1230909290b": {
         "workload": (128, 32768, 64),
-        "kernel": "gram_kernel<GramShape<64, 4, 4, 256, 2>, score>",
-        # FETCH_SIZE 1875232.2 KiB x 1.99994 (a 1 GiB copy reads 524302.6 KiB),
-        # WRITE_SIZE 114688.0 KiB x 1.0 (the same copy writes 1048576 KiB)
-        "fetch_bytes": 3840368895,
-        "write_bytes": 117440512,
-        "bytes_per_launch": 3957809407,
+        "kernel": "tri_sweep_kernel<GramShape<64, 3, 4, 256, 2>>",
+        # FETCH_SIZE 2469692.9 KiB x 1.99994 (a 1 GiB copy reads 524302.6 KiB),
+        # WRITE_SIZE 1493516.9 KiB x 1.0 (the same copy writes 1048576 KiB)
+        "fetch_bytes": 5057790411,
+        "write_bytes": 1529361280,
+        "bytes_per_launch": 6587151691,
     },
 }
 
@@ -232,9 +243,15 @@ def main():
 
     # the oracle on the host cores first, before anything initialises the GPU
     cpu = None
+    cpu_note = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, overrides, cap_list)
-        print(f"# cpu baseline: {cpu['sample']}", file=sys.stderr, flush=True)
+        if N > CPU_BASELINE_MAX_N:
+            cpu_note = (f"not run: the oracle's step is O(N^2 d) fp64 work per head, so one whole head at N={N} "
+                        f"costs {(N / CPU_BASELINE_MAX_N) ** 2:.0f}x an N={CPU_BASELINE_MAX_N} head (15-20 s on one "
+                        f"host core), several minutes")
+        else:
+            cpu = cpu_baseline(cfg, overrides, cap_list)
+            print(f"# cpu baseline: {cpu['sample']}", file=sys.stderr, flush=True)
 
     import torch
 
@@ -299,7 +316,7 @@ def main():
     phases = {}
     if not repair_mode:
         phases["norms_energy"] = avg(lambda e: e[0].elapsed_ms(0, 1))
-        phases["gram_score"] = avg(lambda e: e[0].elapsed_ms(1, 2))
+        phases["score_sweep"] = avg(lambda e: e[0].elapsed_ms(1, 2))
         phases["score_resolve"] = avg(lambda e: e[0].elapsed_ms(2, 3))
         phases["select"] = avg(lambda e: e[1].elapsed_ms(0, 1))
     phases["repair_norms"] = avg(lambda e: e[2].elapsed_ms(0, 1))
@@ -346,15 +363,15 @@ def main():
     if repair_mode:
         dom_ms = phases["repair_gram"]
         alg = rgram
-        kernel = f"gram_kernel<{REPAIR_SHAPE[d]}, repair>"
+        kernel = REPAIR_KERNEL[d]
     else:
-        dom_ms = phases["gram_score"]
+        dom_ms = phases["score_sweep"]
         alg = algorithmic_gram_flops(N, d, cfg.window, G)
-        kernel = f"gram_kernel<{SCORE_SHAPE[d]}, score>"
+        kernel = SCORE_KERNEL[d]
     achieved = alg / (dom_ms * 1e-3) / 1e12
 
     traffic = None
-    meas = MEASURED_TRAFFIC.get(source_hash(GRAM_SOURCE))
+    meas = MEASURED_TRAFFIC.get(source_hash(SOURCES["repair" if repair_mode else "score"]))
     if meas is not None and meas.get("workload") == (G, N, d) and meas.get("kernel") == kernel:
         traffic = meas["bytes_per_launch"]
 
@@ -405,6 +422,9 @@ def main():
         line.update(extras)
     if cpu is not None:
         line["cpu_baseline"] = {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    elif cpu_note is not None:
+        line["cpu_baseline"] = None
+        line["cpu_baseline_note"] = cpu_note
     print(json.dumps(line), flush=True)
     if args.results_dir:
         os.makedirs(args.results_dir, exist_ok=True)
