@@ -49,3 +49,34 @@ def test_golden_records_recompute(cfg_id, head):
     stored = dict(stored)
     stored.pop("seconds")
     assert json.loads(json.dumps(rec)) == stored
+
+
+def test_swap_rule_matches_the_oracle_repair():
+    """The swap rule the GPU tests use to judge a near-tie pick gives the
+    oracle's repair when fed the oracle's own b(S0); a substituted b that
+    crosses tau or reorders a ranking is reported as a change."""
+    import numpy as np
+
+    from oracle import twinkv_oracle as O
+    from synth import gumbel_retained, make_head
+
+    cfg = get_config(1)
+    h = make_head(cfg, 0)
+    K = O.widen_bf16(h["K"])
+    S0 = gumbel_retained(cfg, 0)
+    ref = O.repair_head(K, S0, cfg.tau, cfg.window, cfg.sink, cfg.recent)
+    got = PR.swap_rule(ref["best"], S0, cfg.tau, cfg.sink, cfg.recent)
+    assert (got["n_orphans"], got["n_donors"], got["m"]) == (ref["n_orphans"], ref["n_donors"], ref["m"])
+    assert np.array_equal(got["pairs"], ref["pairs"]) and np.array_equal(got["keep"], ref["keep"] != 0)
+    b = ref["best"]
+    assert not PR.near_tie_effect(b, {}, S0, cfg.tau, cfg.sink, cfg.recent)["swap_changes"]
+    assert not PR.near_tie_effect(b, {0: float(b[0])}, S0, cfg.tau, cfg.sink, cfg.recent)["swap_changes"]
+    orphans = ref["orphans"]
+    assert ref["m"] >= 2
+    first, second = int(orphans[0]), int(orphans[1])
+    # the first-ranked orphan pushed past the second reorders the pairs
+    eff = PR.near_tie_effect(b, {first: float(b[second]) + 1e-12}, S0, cfg.tau, cfg.sink, cfg.recent)
+    assert eff["swap_changes"] and eff["class_changes"] == 0
+    # an orphan lifted over tau leaves O
+    eff = PR.near_tie_effect(b, {first: cfg.tau}, S0, cfg.tau, cfg.sink, cfg.recent)
+    assert eff["swap_changes"] and eff["class_changes"] == 1

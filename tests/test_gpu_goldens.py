@@ -81,9 +81,9 @@ def _check_picks(gpu_arg, near, K, n, best_sim_gpu, tag, allowed=None):
     """Near-tie rows: the GPU's pick is a stored candidate (eligible and within
     NEAR_TIE of the maximum), and not an exact tie of the maximum other than
     the lowest position.  Returns the arg array with those rows masked and the
-    rows whose pick differs from the oracle's."""
+    oracle's maximum at each row whose pick differs from the oracle's."""
     masked = gpu_arg.astype(np.int64).copy()
-    differs = []
+    differs = {}
     for key, cand in near.items():
         r = int(key)
         cand = cand["cand"] if isinstance(cand, dict) else cand
@@ -98,12 +98,12 @@ def _check_picks(gpu_arg, near, K, n, best_sim_gpu, tag, allowed=None):
         assert pick_sim < top or j == lowest_top, f"{tag} row {r}: pick {j} ties the maximum but is not the lowest"
         assert abs(best_sim_gpu[r] - pick_sim) <= PR.EXACT_SIM_RTOL * abs(pick_sim), f"{tag} row {r}: reported sim"
         if j != lowest_top:  # the oracle's pick: the lowest position attaining the maximum
-            differs.append(r)
+            differs[r] = float(top)
         masked[r] = -2
     return masked, differs
 
 
-def _check_repair(gold, rep, g_local, K, n, S0, tag, tally):
+def _check_repair(gold, rep, g_local, K, n, S0, tag, tally, tau, sink, recent):
     gr = gold
     arg = rep["best_idx"][g_local].cpu().numpy()
     best = rep["best_sim"][g_local].cpu().numpy()
@@ -112,19 +112,25 @@ def _check_repair(gold, rep, g_local, K, n, S0, tag, tally):
     np.testing.assert_allclose(best, _pairs_sim(K, n, rows, arg.astype(np.int64)), rtol=PR.EXACT_SIM_RTOL, atol=0,
                                err_msg=f"{tag} b(S0) against the exact cosine of the reported pair")
     _chunks_equal(MG.chunk_digests(masked), gr["arg_chunks"], "b(S0) positions", tag)
-    ambiguous = sum(1 for r in differs if gr["near_tie"][str(r)]["near_tau"])
-    affected = sum(1 for r in differs if gr["near_tie"][str(r)]["in_od"])
-    rep_c = {"repair_heads": 1, "repair_near_tie_differs": len(differs), "repair_class_ambiguous": ambiguous,
-             "repair_rank_affected": affected}
-    if not ambiguous:
+    # a near-tie pick changes the swap only if the swap rule, applied to the
+    # GPU's b with the oracle's maxima put back at those rows, gives another
+    # result; otherwise |O|, |D|, m, S1 and the pairs must be the oracle's
+    effect = PR.near_tie_effect(best, differs, S0, tau, sink, recent)
+    rep_c = {"repair_heads": 1, "repair_near_tie_differs": len(differs),
+             "repair_class_ambiguous": effect["class_changes"], "repair_rank_affected": int(effect["swap_changes"])}
+    if not effect["swap_changes"]:
         got = [int(rep[k][g_local]) for k in ("n_orphans", "n_donors", "n_swaps")]
         assert got == [gr["n_orphans"], gr["n_donors"], gr["m"]], f"{tag}: |O|, |D|, m {got} vs oracle"
-    if not ambiguous and not affected:
         m = gr["m"]
         pairs = rep["pairs"][g_local].cpu().numpy()
         assert MG.digest(np.packbits(rep["keep"][g_local].cpu().numpy())) == gr["keep"], f"{tag}: S1"
         assert MG.digest(np.ascontiguousarray(pairs[:m], dtype="<i4")) == gr["pairs"], f"{tag}: swap pairs"
         assert np.all(pairs[m:] == -1), f"{tag}: pair padding"
+    else:
+        _say(f"[{tag}] a near-tie pick of b(S0) changes the swap; checking it follows from the GPU's own b")
+        gpu = {k: rep[k][g_local].cpu().numpy() for k in ("keep", "n_orphans", "n_donors", "n_swaps", "pairs")}
+        gpu["best"] = best
+        PR.check_swap_follows(gpu, S0, tau, sink, recent, tag)
     tally.add(rep_c)
     return rep_c
 
@@ -161,7 +167,8 @@ def _run_workload(cfg_id):
         n = O.squared_norms(Kf)
         hrec = {"inputs": h["inputs"][:16]}
         if cfg.mode == "repair":
-            hrec.update(_check_repair(h["repair"], rep, gl, Kf, n, S0[gl] != 0, tag, tally))
+            hrec.update(_check_repair(h["repair"], rep, gl, Kf, n, S0[gl] != 0, tag, tally,
+                                      cfg.tau, cfg.sink, cfg.recent))
         else:
             count = res["count"][gl].cpu().numpy()
             arg = res["best_idx"][gl].cpu().numpy()
@@ -196,7 +203,8 @@ def _run_workload(cfg_id):
             hrec.update(rc)
             if exact:
                 keep_o = sel["keep"][gl].cpu().numpy() != 0  # certified equal to the oracle's selection
-                hrec.update(_check_repair(h["repair"], rep, gl, Kf, n, keep_o, tag + " repair", tally))
+                hrec.update(_check_repair(h["repair"], rep, gl, Kf, n, keep_o, tag + " repair", tally,
+                                          cfg.tau, cfg.sink, cfg.recent))
         record["heads"][str(g)] = hrec
     totals = tally.check()
     record["exclusions"] = totals
