@@ -71,8 +71,8 @@ SOURCES = {"score": os.path.join(ROOT, "key_redundancy_scoring_amd", "csrc", "tr
 # the dominant kernel of each mode per head dim, as the kernel trace names it
 SCORE_KERNEL = {64: "tri_sweep_kernel<GramShape<64, 3, 4, 256, 2>>",
                 128: "tri_sweep_kernel<GramShape<128, 2, 4, 128, 2>>"}
-REPAIR_KERNEL = {64: "gram_kernel<GramShape<64, 2, 4, 128, 3>, repair>",
-                 128: "gram_kernel<GramShape<128, 2, 4, 128, 2>, repair>"}
+REPAIR_KERNEL = {64: "gram_kernel<GramShape<64, 2, 4, 128, 3>>",
+                 128: "gram_kernel<GramShape<128, 2, 4, 128, 2>>"}
 
 # HBM traffic of one launch of the dominant kernel, from rocprofv3 FETCH_SIZE /
 # WRITE_SIZE (KiB per dispatch) scaled by the counters' reading for a plain

@@ -472,10 +472,9 @@ int twinkv_repair(const twinkv_params* p, const void* keys, const uint8_t* keep_
   ga.N = p->N;
   ga.d = p->d;
   ga.window = kernel_window(p);
-  ga.tau = p->tau;
   ga.best_sim = best_sim;
   ga.best_idx = best_idx;
-  TRY_HIP(launch_gram(ga, GRAM_REPAIR, stream));
+  TRY_HIP(launch_gram(ga, stream));
   TRY(record(marks, 3, stream));
   SwapArgs sw{};
   sw.keep_in = keep_in;

@@ -1,31 +1,23 @@
-// Fused Gram sweep: for every row i of a head, reduce the row of cosine
-// similarities against a column set to
-//   * the nonlocal twin count c_i = #{ j : |i-j| > w, sim(i,j) > tau }
-//     ("TwinKV: A Composable Repair Pass ...", section 3.2, Eq. 2; "Small
-//     Frequency Corrections ...", section 3.2), score mode only;
-//   * the best nonlocal twin b_i = max sim(i,j) over the same j and its lowest
-//     position a_i; in repair mode the columns are the retained set S0, which
-//     gives b_i(S0) of Eq. 4 ("TwinKV ...", section 3.4), for the rows of a
-//     given list (all rows, or those whose unrestricted best twin was not
-//     retained);
-// and, in score mode, the discounted score e_i * ln((N+1)/(c_i+1)) ("Small
-// Frequency Corrections ...", section 3.2).  The N x N similarity matrix is
-// never written anywhere.
+// Restricted Gram sweep of the repair pass: for every listed row i of a head,
+// the best surviving twin b_i(S0) = max sim(i, j) over the retained columns
+// j in S0 with |i - j| > w, and its lowest position a_i(S0) ("TwinKV: A
+// Composable Repair Pass ...", section 3.4, Eq. 4).  The rows are all
+// positions, or those whose unrestricted best twin was not retained.  This
+// is the O(nKd) form of that section: rows meet only the K retained columns,
+// and the similarity matrix is never written anywhere.
 //
 // Mapping onto gfx950:
-//   * A workgroup of WAVES waves owns WAVES*RB*32 consecutive rows of one head
-//     (in repair mode, consecutive entries of the row list: their positions
-//     ascend, and the band test below uses the first and last of a wave);
-//     each wave owns RB blocks of 32 rows whose bf16 keys stay in VGPRs as
-//     MFMA B operands for the whole sweep.  Two workgroups share a CU (three
-//     in the repair shape), so one workgroup's prologue and fp64 fixup
-//     overlap another's sweep.
-//   * Column keys stream HBM/L2 -> LDS in stages of SC columns with
+//   * A workgroup of WAVES waves owns WAVES*RB*32 consecutive entries of the
+//     row list (their positions ascend, and the band test below uses the
+//     first and last of a wave); each wave owns RB blocks of 32 rows whose
+//     bf16 keys stay in VGPRs as MFMA B operands for the whole sweep.  Three
+//     workgroups share a CU at d = 64 (two at d = 128), so one workgroup's
+//     prologue and fp64 fixup overlap another's sweep.
+//   * Column keys (a compacted copy of the retained keys, with their
+//     positions) stream HBM/L2 -> LDS in stages of SC columns with
 //     global_load_lds (no VGPR round trip), into two LDS buffers: stage s+1
 //     is in flight while stage s is computed, and the one wait per stage sits
-//     before the barrier.  Columns are contiguous rows of a key array: the
-//     head's own keys in score mode, a compacted copy of the retained keys in
-//     repair mode.  Each lane of a direct load writes 16 bytes at
+//     before the barrier.  Each lane of a direct load writes 16 bytes at
 //     base + 16*lane, so the XOR swizzle that spreads the MFMA A-operand reads
 //     over the LDS banks (16-byte chunk k of column c sits at slot
 //     c*CH + (k ^ swz(c))) is applied by choosing which global chunk each
@@ -38,12 +30,10 @@
 //   * Epilogue per 32x32 block and lane, in registers: y = dot * (1/||k_j||)
 //     (16 multiplies), the block maximum by a 3-input max tree, then one
 //     compare and two selects keep (running max, first tile attaining it).
-//     The count needs y > tau*||k_i||; the 16 compares run only when some
-//     lane's block maximum crosses that threshold (rare: twins are sparse).
 //   * Tiles that touch the |i-j| <= w band or the ragged tail (a few per row
 //     block) leave the state unchanged in the sweep (branch-free: their
 //     maximum is taken as -inf) and are recomputed with masking at the end of
-//     their stage, in tile order; there an exact tie with the running maximum
+//     the sweep, in tile order; there an exact tie with the running maximum
 //     goes to the lower tile, as it would in column order.
 //   * Which of the 16 columns of the winning tile holds the maximum is not
 //     tracked in the sweep; after it, a lane whose half-row maximum can be the
@@ -59,40 +49,18 @@
 
 #include "sweep.h"
 
-#ifndef TWINKV_GRAM64_RB
-#define TWINKV_GRAM64_RB 4
-#endif
-#ifndef TWINKV_GRAM64_WAVES
-#define TWINKV_GRAM64_WAVES 4
-#endif
-#ifndef TWINKV_GRAM64_SC
-#define TWINKV_GRAM64_SC 256
-#endif
-#ifndef TWINKV_GRAM128_RB
-#define TWINKV_GRAM128_RB 2
-#endif
-#ifndef TWINKV_GRAM128_WAVES
-#define TWINKV_GRAM128_WAVES 4
-#endif
-#ifndef TWINKV_GRAM128_SC
-#define TWINKV_GRAM128_SC 128
-#endif
-
 namespace twinkv {
 namespace {
 
-// score mode at d = 64: four row blocks per wave, so each staged column
-// feeds 128 rows of the wave; about 240 VGPRs, two waves per SIMD
-using Shape64 = GramShape<64, TWINKV_GRAM64_RB, TWINKV_GRAM64_WAVES, TWINKV_GRAM64_SC, 2>;
-// repair mode at d = 64: two row blocks per wave at three waves per SIMD (at
-// most 168 VGPRs).  The restricted sweep covers only the retained columns,
-// often a few thousand, so the per-workgroup tail (masked tiles, fixup) weighs
-// more, and a third wave per SIMD hides it better than the column reuse of
-// four row blocks pays
-using Shape64Short = GramShape<64, 2, 4, 128, 3>;
-using Shape128 = GramShape<128, TWINKV_GRAM128_RB, TWINKV_GRAM128_WAVES, TWINKV_GRAM128_SC, 2>;
+// d = 64: two row blocks per wave at three waves per SIMD (at most 168
+// VGPRs).  The restricted sweep covers only the retained columns, often a
+// few thousand, so the per-workgroup tail (masked tiles, fixup) weighs more,
+// and a third wave per SIMD hides it better than the column reuse of four
+// row blocks pays
+using Shape64 = GramShape<64, 2, 4, 128, 3>;
+using Shape128 = GramShape<128, 2, 4, 128, 2>;
 
-template <class S, int MODE>
+template <class S>
 __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a) {
   constexpr int D = S::D;
   constexpr int RB = S::RB;
@@ -131,19 +99,19 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
   const uint4* Kg = reinterpret_cast<const uint4*>(a.keys) + (size_t)g * N * CH;
   const uint4* Cg = reinterpret_cast<const uint4*>(a.col_keys) + (size_t)g * N * CH;
   const float* crinv_g = a.col_rinv + (size_t)g * N;
-  const int32_t* cpos_g = (MODE == GRAM_REPAIR) ? a.col_pos + (size_t)g * N : nullptr;
-  const int ncols = (MODE == GRAM_REPAIR) ? a.ncols[g] : (int)N;
-  // repair mode sweeps the rows listed in row_pos (ascending positions); row
-  // r of the list is position row_of(r), clamped to the last listed row
-  const int nrows = (MODE == GRAM_REPAIR) ? a.nrows[g] : (int)N;
+  const int32_t* cpos_g = a.col_pos + (size_t)g * N;
+  const int ncols = a.ncols[g];
+  // the rows listed in row_pos (ascending positions); row r of the list is
+  // position row_of(r), clamped to the last listed row
+  const int nrows = a.nrows[g];
   if ((int64_t)rb * ROWS >= nrows) return;  // the whole workgroup, before any barrier
-  const int32_t* rpos_g = (MODE == GRAM_REPAIR) ? a.row_pos + (size_t)g * N : nullptr;
-  auto row_of = [&](int r) TWINKV_INLINE { return (MODE == GRAM_REPAIR) ? rpos_g[r < nrows ? r : nrows - 1] : r; };
+  const int32_t* rpos_g = a.row_pos + (size_t)g * N;
+  auto row_of = [&](int r) TWINKV_INLINE { return rpos_g[r < nrows ? r : nrows - 1]; };
 
   // ---- row keys as MFMA B operands, row state
   bf16x8 brow[RB][KS];
-  float thr[RB], best[RB];
-  int btile[RB], cnt[RB];
+  float best[RB];
+  int btile[RB];
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     const int r = row0 + 32 * b + lrow;
@@ -154,12 +122,8 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
       if (r < nrows) v = Kg[(size_t)i * CH + 2 * s + h];
       brow[b][s] = __builtin_bit_cast(bf16x8, v);
     }
-    // + 0.0f turns a -0 threshold (tau = -0, or a zero key with tau < 0) into +0
-    thr[b] = (r < nrows && MODE == GRAM_SCORE) ? (float)(a.tau * sqrt(a.nsq[(size_t)g * N + i])) + 0.0f
-                                               : __builtin_inff();
     best[b] = -__builtin_inff();
     btile[b] = -1;
-    cnt[b] = 0;
   }
 
   // ---- byte offsets of this lane's stage loads and A-operand reads.  Load t
@@ -192,7 +156,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
       for (int t = 0; t < LOADS; ++t) dma16(base + (size_t)NT * 16 * t + ld_off[t & 1], &sb.keys[NT * t + wave * 64]);
       if (wave < SC / 64) {
         dma4(crinv_g + col0 + tid, &sb.rinv[wave * 64]);
-        if (MODE == GRAM_REPAIR) dma4(cpos_g + col0 + tid, &sb.pos[wave * 64]);
+        dma4(cpos_g + col0 + tid, &sb.pos[wave * 64]);
       }
       return;
     }
@@ -208,7 +172,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
     if (wave < SC / 64) {
       const int col = col0 + tid < lastc ? col0 + tid : lastc;
       dma4(crinv_g + col, &sb.rinv[wave * 64]);
-      if (MODE == GRAM_REPAIR) dma4(cpos_g + col, &sb.pos[wave * 64]);
+      dma4(cpos_g + col, &sb.pos[wave * 64]);
     }
   };
 
@@ -240,14 +204,8 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
 #pragma unroll
     for (int tt = 0; tt < TILES; ++tt) {
       const int c0 = (st * TILES + tt) * 32;
-      int pmin, pmax;
-      if (MODE == GRAM_REPAIR) {
-        pmin = __builtin_amdgcn_readfirstlane(sb.pos[tt * 32]);
-        pmax = __builtin_amdgcn_readfirstlane(sb.pos[tt * 32 + 31]);
-      } else {
-        pmin = c0;
-        pmax = c0 + 31;
-      }
+      const int pmin = __builtin_amdgcn_readfirstlane(sb.pos[tt * 32]);
+      const int pmax = __builtin_amdgcn_readfirstlane(sb.pos[tt * 32 + 31]);
       const bool mk = (c0 + 31 >= ncols) || (pmin <= rhi + w && pmax >= rlo - w);
       bits |= (unsigned)mk << tt;
     }
@@ -260,23 +218,14 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
     for (int tt = 0; tt < TILES; ++tt) bits |= (unsigned)((st * TILES + tt) * 32 + 31 >= ncols) << tt;
     return bits;
   };
-  // count of y > tau*||k_i|| over the 16 values of a block
-  // (y > thr read off the sign bit of thr - y: there are no NaNs, thr is
-  // never -0, and a zero difference is +0; no compare-to-carry hazards)
-  auto count16 = [&](const f32x16& y, int b) TWINKV_INLINE {
-    uint32_t c = 0;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) c += __float_as_uint(thr[b] - y[r]) >> 31;
-    cnt[b] += (int)c;
-  };
   auto mfma_block = [&](const bf16x8 (&A)[KS], int b, f32x16& acc) TWINKV_INLINE {
     acc = (f32x16){};
 #pragma unroll
     for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], brow[b][s], acc, 0, 0, 0);
   };
   // Epilogue of block b of a tile whose dots are in acc: y = dot * rinv_j, the
-  // block maximum (neutralised to -inf on a masked tile by neg), running
-  // maximum and first tile, count when some lane crosses tau*||k_i||.
+  // block maximum, running maximum and first tile (a masked tile leaves the
+  // state alone).
   auto epilogue = [&](f32x16& acc, int b, const float (&rv)[16], bool live, int tile) TWINKV_INLINE {
     float yy[16];
 #pragma unroll
@@ -288,9 +237,6 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
     if (live) {  // wave-uniform: a masked tile leaves the state alone
       btile[b] = m > best[b] ? tile : btile[b];
       best[b] = __builtin_fmaxf(best[b], m);
-      if (MODE == GRAM_SCORE) {
-        if (__ballot(m > thr[b]) != 0ull) count16(acc, b);
-      }
     }
   };
   // Keep the next tile's MFMAs between the epilogue's vector instructions.
@@ -401,7 +347,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
         cval[r] = col < ncols;
         const int cc = cval[r] ? col : ncols - 1;
         rvm[r] = crinv_g[cc];
-        jpos[r] = (MODE == GRAM_REPAIR) ? cpos_g[cc] : col;
+        jpos[r] = cpos_g[cc];
       }
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
@@ -420,7 +366,6 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
           best[b] = m;
           btile[b] = t;
         }
-        if (MODE == GRAM_SCORE) count16(y, b);
       }
     }
   }
@@ -478,7 +423,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
           for (int u = 0; u < BATCH; ++u) {
             const int col = tp * 32 + tile_col(r0 + u, p);
             const int cc = col < ncols ? col : ncols - 1;
-            const int j = (MODE == GRAM_REPAIR) ? cpos_g[cc] : cc;
+            const int j = cpos_g[cc];
             const uint4* kj = Kg + (size_t)j * CH;
 #pragma unroll
             for (int s2 = 0; s2 < KS; ++s2) q[u][s2] = kj[2 * s2 + h];
@@ -488,7 +433,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
           for (int u = 0; u < BATCH; ++u) {
             const int col = tp * 32 + tile_col(r0 + u, p);
             const int cc = col < ncols ? col : ncols - 1;
-            const int j = (MODE == GRAM_REPAIR) ? cpos_g[cc] : cc;
+            const int j = cpos_g[cc];
             const int dist = i > j ? i - j : j - i;
             float part = 0.0f;
 #pragma unroll
@@ -513,7 +458,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
           const int r = __builtin_ctz(cm);
           cm &= cm - 1u;
           const int col = tp * 32 + 8 * (r >> 2) + 4 * p + (r & 3);
-          const int j = (MODE == GRAM_REPAIR) ? cpos_g[col] : col;
+          const int j = cpos_g[col];
           const uint4* kj = Kg + (size_t)j * CH;
           double part = 0.0;
 #pragma unroll
@@ -529,44 +474,28 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
         }
       }
     }
-    int c = 0;
-    if (MODE == GRAM_SCORE) c = cnt[b] + __shfl_xor(cnt[b], 32);
     if (h == 0 && row_ok) {
       const size_t o = (size_t)g * N + i;
       a.best_sim[o] = bb;
       a.best_idx[o] = aa;
-      if (MODE == GRAM_SCORE) {
-        if (a.tau < 0.0 && a.nsq[o] == 0.0) {
-          // a zero key has cosine 0 with every key: all nonlocal positions count
-          const int64_t lo = i - w > 0 ? i - w : 0;
-          const int64_t hi = i + w < N - 1 ? i + w : N - 1;
-          c = (int)(N - (hi - lo + 1));
-        }
-        a.count[o] = c;
-        const double disc = log((double)(N + 1) / (double)(c + 1));
-        a.score[o] = a.energy[o] * disc;
-        if (a.omega) a.omega[o] = disc / log((double)(N + 1));
-      }
     }
   }
 }
 
-template <class S, int MODE>
+template <class S>
 hipError_t launch_dm(const GramArgs& a, hipStream_t stream) {
   const int64_t bph = (a.N + S::ROWS - 1) / S::ROWS;
   const int64_t total = a.G * bph;
   const int64_t grid = 8 * ((total + 7) / 8);
   if (grid > INT_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gram_kernel<S, MODE>), dim3((unsigned)grid), dim3(64 * S::WAVES), 0, stream, a);
+  hipLaunchKernelGGL((gram_kernel<S>), dim3((unsigned)grid), dim3(64 * S::WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gram(const GramArgs& a, int mode, hipStream_t stream) {
-  if (a.d == 64)
-    return mode == GRAM_SCORE ? launch_dm<Shape64, GRAM_SCORE>(a, stream) : launch_dm<Shape64Short, GRAM_REPAIR>(a, stream);
-  return mode == GRAM_SCORE ? launch_dm<Shape128, GRAM_SCORE>(a, stream) : launch_dm<Shape128, GRAM_REPAIR>(a, stream);
+hipError_t launch_gram(const GramArgs& a, hipStream_t stream) {
+  return a.d == 64 ? launch_dm<Shape64>(a, stream) : launch_dm<Shape128>(a, stream);
 }
 
 }  // namespace twinkv

@@ -7,34 +7,27 @@
 
 namespace twinkv {
 
-// Column source for the Gram sweep.
-enum GramMode { GRAM_SCORE = 0, GRAM_REPAIR = 1 };
-
+// Restricted Gram sweep of the repair pass (gram.hip).
 struct GramArgs {
   const uint16_t* keys;      // bf16 [G][N][d]: the rows (and the fp64 fixup's operands)
   const double* nsq;         // ||k||^2 in fp64 [G][N]
-  const uint16_t* col_keys;  // bf16 [G][N][d]: the streamed columns (score: keys; repair: S0 compacted)
+  const uint16_t* col_keys;  // bf16 [G][N][d]: the retained keys, compacted in position order
   const float* col_rinv;     // 1/||k|| in fp32 of each column [G][N] (0 for a zero key)
-  const int32_t* col_pos;    // repair: original position of each compacted column, ascending [G][N]
-  const int32_t* ncols;      // repair: number of retained positions per head [G]
-  const int32_t* row_pos;    // repair: positions of the rows to sweep, ascending [G][N]
-  const int32_t* nrows;      // repair: number of rows to sweep per head [G]
-  const double* energy;   // score: ||v||^2 [G][N]
+  const int32_t* col_pos;    // original position of each compacted column, ascending [G][N]
+  const int32_t* ncols;      // number of retained positions per head [G]
+  const int32_t* row_pos;    // positions of the rows to sweep, ascending [G][N]
+  const int32_t* nrows;      // number of rows to sweep per head [G]
   int64_t G, N;
   int32_t d, window;
-  double tau;
   // outputs
-  int32_t* count;         // score only
   double* best_sim;
   int32_t* best_idx;
-  double* score;          // score only
-  double* omega;          // score only, may be null
 };
 
 // Single-order score sweep (tri.hip).  Each unordered nonlocal pair is
 // computed once, in the workgroup of its lower position's row block: the
 // row side (the lower position's maximum over later columns) is tracked per
-// row as in the two-order sweep, the column side (each later position's
+// row in registers, the column side (each later position's
 // maximum over the block's rows) is reduced across lanes and stored per
 // (row block, column), and a resolve pass finds the exact best twin.
 struct TriArgs {
@@ -76,7 +69,7 @@ hipError_t launch_tri(const TriArgs& a, hipStream_t stream, hipEvent_t mark);
 // ||v||^2 (fp64; skipped when values is null).
 hipError_t launch_norms(const uint16_t* keys, const uint16_t* values, int64_t nkeys, int d, double* nsq,
                         float* rinv, double* energy, hipStream_t stream);
-hipError_t launch_gram(const GramArgs& a, int mode, hipStream_t stream);
+hipError_t launch_gram(const GramArgs& a, hipStream_t stream);
 
 
 struct SelectArgs {

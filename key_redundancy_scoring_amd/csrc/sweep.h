@@ -1,5 +1,5 @@
-// Building blocks shared by the Gram sweeps (gram.hip: the repair-mode and
-// two-order sweeps; tri.hip: the single-order score sweep): launch shapes,
+// Building blocks shared by the Gram sweeps (gram.hip: the repair pass's
+// restricted sweep; tri.hip: the single-order score sweep): launch shapes,
 // LDS stage buffers filled by direct global->LDS loads, the XOR swizzle of
 // the MFMA A-operand reads, the accumulator layout of
 // v_mfma_f32_32x32x16_bf16 and exact fp64 dot products of bf16 chunks.

@@ -9,7 +9,7 @@
 // row block, which sweeps the columns from its own first row to the end.
 // Its value serves both ends:
 //   * the row side (i's maximum over later j, the count of i) stays in the
-//     lane that holds row i, as in the two-order sweep: y = dot / ||k_j||,
+//     lane that holds row i, as in the repair pass's sweep: y = dot / ||k_j||,
 //     a 3-input max tree per 32x32 block and a running (maximum, first tile)
 //     per half-row;
 //   * the column side (j's maximum over the block's rows) is scaled to the
@@ -117,8 +117,8 @@ __device__ __forceinline__ int64_t part_offset(int64_t g, int64_t rb, int64_t N,
 // j = tp*32 + tile_col(r, p), those with j < ncols and |i - j| > w): an fp32
 // screen, then fp64 for those within the margin of the largest.  Both lanes
 // of a row run it (each over the feature chunks 2s+h it holds) and combine
-// partial sums, so they reach identical results.  Positions map through
-// pos_of (identity in score mode).
+// partial sums, so they reach identical results.  Column index c is
+// position pos_of(c).
 template <int D, class PosOf>
 __device__ __forceinline__ void exact_tile(const uint4* Kg, const double* nsq_g, const float* rinv_g, int i, double ni,
                                            int tp, int p, int ncols, int w, int h, float margin, PosOf pos_of,
@@ -232,7 +232,9 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
   const double* nsq_g = a.nsq + (size_t)g * N;
   int32_t* ccount_g = a.ccount + (size_t)g * N;
 
-  // stage-load and A-operand offsets (see the two-order sweep)
+  // stage-load and A-operand offsets: load t of a stage reads column
+  // (tid + NT*t)/CH at a swizzled chunk, the A operand of tile tt reads column
+  // 32*tt + lrow; both depend per lane only on the parity of t or tt
   static_assert((2 * NT / CH) % (CH == 8 ? 64 : 16) == 0 && 64 % (CH == 8 ? 64 : 16) == 0, "swizzle period");
   uint32_t ld_off[2];
   uint32_t a_off[2][KS];
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
     // w for some row of the workgroup (the diagonal) and a ragged last stage
     // run tile by tile from LDS, masking pairs with j - i <= w, columns past
     // the end and rows past the end; the clean stages between them (every tile
-    // past the band of every row) run the rolling pipeline of the two-order
+    // past the band of every row) run the rolling pipeline of the repair
     // sweep unmasked.  Tiles are visited in column order, so the first tile
     // attaining a row's maximum is kept.
     const int nstages = (ncols + SC - 1) / SC;

@@ -1,6 +1,6 @@
 """The work counts behind the benchmark's roofline figures, against brute force.
 
-The roofline's `achieved` divides the algorithmic work of one score-mode Gram
+The roofline's `achieved` divides the algorithmic work of one score-sweep
 launch by its time: one d-length dot product (2d flop) per unordered pair
 (i, j) with j - i > window, since a pair counts for both i and j ("TwinKV: A
 Composable Repair Pass ...", section 3.2, Eq. 2).  The repair figure counts
