@@ -21,7 +21,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libtwinkv.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "norms.hip", "gram.hip", "tri.hip", "select.hip", "repair.hip", "gather.hip", "alloc.hip", "stats.hip"]
+SOURCES = ["api.hip", "norms.hip", "gram.hip", "tri.hip", "resolve.hip", "select.hip", "repair.hip", "gather.hip", "alloc.hip", "stats.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}",

@@ -54,9 +54,17 @@ struct Carve {
   }
 };
 
+// Candidate lists of the exact resolve: rows, columns, counts per head.
+size_t cand_ws(const twinkv_params* p) {
+  const size_t cap = (size_t)p->G * (size_t)rowres_cand_cap(p->N);
+  return 2 * align_up(cap * sizeof(int32_t)) + align_up((size_t)p->G * sizeof(int32_t));
+}
+
 // Score workspace: squared norms, inverse norms, then the single-order
 // sweep's column maxima, row-side results, column counts, packed best twins,
-// overall maxima and candidate bits (carved in this order by score_carve).
+// overall maxima, candidate bits, the queue of rows for the exact resolve
+// (positions, thresholds, counts) and its candidate list, carved in this
+// order by score_launch.
 size_t score_ws(const twinkv_params* p) {
   const size_t G = (size_t)p->G, N = (size_t)p->N;
   const size_t n = G * N;
@@ -65,15 +73,29 @@ size_t score_ws(const twinkv_params* p) {
   const size_t words = (N + 31) / 32;
   return align_up(n * sizeof(double)) + align_up(n * sizeof(float)) +
          align_up(G * (size_t)tri_part_per_head(p->N, rows) * sizeof(int32_t)) + 3 * align_up(n * sizeof(int32_t)) +
-         align_up(n * sizeof(uint64_t)) + align_up(n * sizeof(float)) + align_up(G * nb * words * sizeof(uint32_t));
+         align_up(n * sizeof(uint64_t)) + align_up(n * sizeof(float)) + align_up(G * nb * words * sizeof(uint32_t)) +
+         align_up(n * sizeof(int32_t)) + align_up(n * sizeof(float)) + align_up(G * sizeof(int32_t)) + cand_ws(p);
 }
 
+// Repair workspace: norms, compacted positions and their counts, rows to
+// sweep and their counts, the swap's key/index scratch (two pairs; the first
+// index array and the second key array also hold the queue of rows for the
+// exact resolve before the swap runs), the compacted keys and their inverse
+// norms, the queue counts and the resolve's candidate list.
 size_t repair_ws(const twinkv_params* p) {
   const size_t n = (size_t)p->G * (size_t)p->N;
   return align_up(n * sizeof(double)) + align_up(n * sizeof(float)) + 2 * align_up(n * sizeof(int32_t)) +
          2 * align_up((size_t)p->G * sizeof(int32_t)) +
          2 * (align_up(n * sizeof(uint64_t)) + align_up(n * sizeof(int32_t))) +
-         align_up(n * (size_t)p->d * sizeof(uint16_t)) + align_up(n * sizeof(float));
+         align_up(n * (size_t)p->d * sizeof(uint16_t)) + align_up(n * sizeof(float)) +
+         align_up((size_t)p->G * sizeof(int32_t)) + cand_ws(p);
+}
+
+// 2^b - 1 for the smallest b with 2^b >= N: the position bits of a packed best.
+uint64_t index_mask(int64_t N) {
+  uint64_t m = 1;
+  while (m < (uint64_t)N) m <<= 1;
+  return m - 1;
 }
 
 struct AllocShape {
@@ -158,6 +180,14 @@ int score_launch(const twinkv_params* p, const void* keys, const void* values, i
   t.nb = (p->N + rows - 1) / rows;
   t.words = (p->N + 31) / 32;
   t.cbits = cv.take<uint32_t>(G * (size_t)t.nb * (size_t)t.words);
+  t.q.row = cv.take<int32_t>(n);
+  t.q.thr = cv.take<float>(n);
+  t.q.count = cv.take<int32_t>(G);
+  t.cand_cap = rowres_cand_cap(p->N);
+  t.cand_row = cv.take<int32_t>(G * (size_t)t.cand_cap);
+  t.cand_col = cv.take<int32_t>(G * (size_t)t.cand_cap);
+  t.cand_count = cv.take<int32_t>(G);
+  t.idx_mask = index_mask(p->N);
   TRY(record(marks, 0, stream));
   TRY_HIP(launch_norms(static_cast<const uint16_t*>(keys), static_cast<const uint16_t*>(values), (int64_t)n, p->d,
                        nsq, rinv, energy, stream));
@@ -450,6 +480,11 @@ int twinkv_repair(const twinkv_params* p, const void* keys, const uint8_t* keep_
   int32_t* idx_b = cv.take<int32_t>(n);
   uint16_t* ckeys = cv.take<uint16_t>(n * (size_t)p->d);
   float* crinv = cv.take<float>(n);
+  int32_t* qcount = cv.take<int32_t>((size_t)p->G);
+  const int64_t cand_cap = rowres_cand_cap(p->N);
+  int32_t* cand_row = cv.take<int32_t>((size_t)p->G * (size_t)cand_cap);
+  int32_t* cand_col = cv.take<int32_t>((size_t)p->G * (size_t)cand_cap);
+  int32_t* cand_count = cv.take<int32_t>((size_t)p->G);
   const uint16_t* kin = static_cast<const uint16_t*>(keys);
 
   TRY(record(marks, 0, stream));
@@ -457,7 +492,7 @@ int twinkv_repair(const twinkv_params* p, const void* keys, const uint8_t* keep_
   TRY(record(marks, 1, stream));
   TRY_HIP(launch_compact(keep_in, p->G, p->N, pos, ncols, stream));
   TRY_HIP(launch_gather(kin, rinv, pos, ncols, p->G, p->N, p->d, ckeys, crinv, stream));
-  TRY_HIP(launch_rows(keep_in, prior_sim, prior_idx, p->G, p->N, row_pos, nrows, best_sim, best_idx, stream));
+  TRY_HIP(launch_rows(keep_in, prior_sim, prior_idx, p->G, p->N, row_pos, nrows, best_sim, best_idx, qcount, stream));
   TRY(record(marks, 2, stream));
   GramArgs ga{};
   ga.keys = kin;
@@ -472,9 +507,34 @@ int twinkv_repair(const twinkv_params* p, const void* keys, const uint8_t* keep_
   ga.N = p->N;
   ga.d = p->d;
   ga.window = kernel_window(p);
+  ga.q.row = idx_a;  // free until the swap
+  ga.q.thr = reinterpret_cast<float*>(keys_b);
+  ga.q.count = qcount;
   ga.best_sim = best_sim;
   ga.best_idx = best_idx;
   TRY_HIP(launch_gram(ga, stream));
+  RowResArgs rr{};
+  rr.keys = kin;
+  rr.nsq = nsq;
+  rr.rinv = rinv;
+  rr.col_keys = ckeys;
+  rr.col_rinv = crinv;
+  rr.col_pos = pos;
+  rr.ncols = ncols;
+  rr.q = ga.q;
+  rr.G = p->G;
+  rr.N = p->N;
+  rr.d = p->d;
+  rr.window = ga.window;
+  rr.best64 = keys_a;  // scratch, free until the swap
+  rr.idx_mask = index_mask(p->N);
+  rr.best_sim = best_sim;
+  rr.best_idx = best_idx;
+  rr.cand_row = cand_row;
+  rr.cand_col = cand_col;
+  rr.cand_count = cand_count;
+  rr.cand_cap = cand_cap;
+  TRY_HIP(launch_rowres(rr, stream));
   TRY(record(marks, 3, stream));
   SwapArgs sw{};
   sw.keep_in = keep_in;

@@ -41,7 +41,10 @@
 //     ones exactly in fp64 (bf16 products are exact), keeping the largest,
 //     lowest position on ties; the two half-waves that share a row then
 //     merge.  This also makes b_i the exact fp64 cosine dot/sqrt(n_i*n_j) of
-//     the chosen pair.
+//     the chosen pair.  The sweep also keeps the largest maximum of the other
+//     tiles; a row where it comes within twice the fp32 error (2e-5 in
+//     cosine units) of the row's maximum is queued for the exact resolve of
+//     resolve.hip, which settles it over every retained column.
 //   * Workgroup ids are remapped so each XCD (ids are dealt round-robin over
 //     8 XCDs) receives a contiguous run of row blocks: the blocks of one head
 //     sweep its key stream together out of one L2.
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
 
   // ---- row keys as MFMA B operands, row state
   bf16x8 brow[RB][KS];
-  float best[RB];
+  float best[RB], second[RB];  // second: the largest maximum of the other tiles
   int btile[RB];
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
@@ -123,6 +126,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
       brow[b][s] = __builtin_bit_cast(bf16x8, v);
     }
     best[b] = -__builtin_inff();
+    second[b] = -__builtin_inff();
     btile[b] = -1;
   }
 
@@ -235,6 +239,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
     }
     const float m = max16(yy);
     if (live) {  // wave-uniform: a masked tile leaves the state alone
+      second[b] = __builtin_amdgcn_fmed3f(m, best[b], second[b]);  // second <= best: max(second, min(m, best))
       btile[b] = m > best[b] ? tile : btile[b];
       best[b] = __builtin_fmaxf(best[b], m);
     }
@@ -362,6 +367,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
           yy[r] = y[r];
         }
         const float m = max16(yy);
+        second[b] = __builtin_amdgcn_fmed3f(m, best[b], second[b]);
         if (m > best[b] || (m == best[b] && t < btile[b])) {
           best[b] = m;
           btile[b] = t;
@@ -474,10 +480,24 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
         }
       }
     }
+    // another tile of either half within twice the fp32 error of the row's
+    // maximum may hold the exact best: queue the row for the exact resolve,
+    // with candidates down to the screening margin below the maximum (in
+    // cosine units).  A zero key is settled here: all its cosines are exactly
+    // 0 and the first tile holds the lowest eligible position.
+    const float ymax = __builtin_fmaxf(best[b], other);
+    const bool near = second[b] >= ymax - 2e-5f * (float)sqrt(ni);
+    const bool near_o = __shfl_xor((int)near, 32) != 0;  // both lanes of the row take part in the shuffle
+    const bool amb = row_ok && ni > 0.0 && ymax > -__builtin_inff() && (near || near_o);
     if (h == 0 && row_ok) {
       const size_t o = (size_t)g * N + i;
       a.best_sim[o] = bb;
       a.best_idx[o] = aa;
+      if (amb) {
+        const int k = atomicAdd(&a.q.count[g], 1);
+        a.q.row[o - i + k] = i;
+        a.q.thr[o - i + k] = (float)((double)ymax / sqrt(ni)) - 8e-5f;
+      }
     }
   }
 }

@@ -7,6 +7,51 @@
 
 namespace twinkv {
 
+// Rows whose best twin the fp32 screen of a sweep cannot settle: another
+// tile than the first one attaining a half-row's maximum comes within twice
+// the fp32 error of it.  Each head's queue holds the positions of such rows
+// and, per entry, the cosine threshold of the candidates to evaluate exactly.
+struct RowQueue {
+  int32_t* row;    // [G][N] queued positions of head g at g*N + k, k < count[g]
+  float* thr;      // [G][N] candidate threshold (cosine) of entry k
+  int32_t* count;  // [G] entries per head; zeroed before the sweep that fills it
+};
+
+// Exact resolve of queued rows (resolve.hip): every column j of the row's
+// column set with |i - j| > w whose fp32 cosine reaches the entry's threshold
+// is evaluated in fp64, the largest (lowest position on ties) wins.
+struct RowResArgs {
+  const uint16_t* keys;      // bf16 [G][N][d]
+  const double* nsq;         // ||k||^2 [G][N]
+  const float* rinv;         // 1/||k|| [G][N]
+  const uint16_t* col_keys;  // bf16 [G][N][d]: the columns (all keys, or the retained keys compacted)
+  const float* col_rinv;     // [G][N] inverse norms of the columns
+  const int32_t* col_pos;    // [G][N] position of each compacted column; null: column c is position c
+  const int32_t* ncols;      // [G] columns per head; null: N
+  RowQueue q;
+  int64_t G, N;
+  int32_t d, window;
+  // outputs: the atomic maximum of each queued row's packed result (positions
+  // in the idx_mask bits) in best64 [G][N]; when best_sim is not null (the
+  // repair pass) best64 is scratch whose queued entries are zeroed first, and
+  // (b, a) of the queued rows are written to best_sim / best_idx at the end
+  uint64_t* best64;
+  uint64_t idx_mask;
+  double* best_sim;
+  int32_t* best_idx;
+  // candidates found by the sweep, evaluated in fp64 by a second kernel:
+  // head g's entry k < min(cand_count[g], cand_cap) is row cand_row[g*cand_cap
+  // + k] and column position cand_col[g*cand_cap + k]; a row with a
+  // candidate past the capacity is evaluated over all its columns instead
+  int32_t* cand_row;
+  int32_t* cand_col;
+  int32_t* cand_count;  // [G]
+  int64_t cand_cap;     // entries per head
+};
+// Candidate-list capacity per head of the exact resolve for N positions.
+int64_t rowres_cand_cap(int64_t N);
+hipError_t launch_rowres(const RowResArgs& a, hipStream_t stream);
+
 // Restricted Gram sweep of the repair pass (gram.hip).
 struct GramArgs {
   const uint16_t* keys;      // bf16 [G][N][d]: the rows (and the fp64 fixup's operands)
@@ -19,6 +64,7 @@ struct GramArgs {
   const int32_t* nrows;      // number of rows to sweep per head [G]
   int64_t G, N;
   int32_t d, window;
+  RowQueue q;  // rows left to the exact resolve (count zeroed by the rows pass)
   // outputs
   double* best_sim;
   int32_t* best_idx;
@@ -39,6 +85,7 @@ struct TriArgs {
   int32_t d, window;
   double tau;
   int64_t nb;            // row blocks per head
+  uint64_t idx_mask;     // 2^b - 1, the smallest with 2^b >= N: position bits of a packed best
   int64_t words;         // 32-bit candidate words per (head, row block): ceil(N/32)
   // workspace
   int32_t* part;         // column maxima per (head, row block), order-preserving fp32 bits; block rb
@@ -49,6 +96,11 @@ struct TriArgs {
   uint64_t* best64;      // [G][N] packed (exact cosine, position) of the best twin found so far; 0 = none
   float* colmax;         // [G][N] fp32 maximum cosine over both sides
   uint32_t* cbits;       // [G][nb][words] candidate row blocks of each position (cleared before the sweep)
+  RowQueue q;            // rows whose row side the sweep cannot settle (count cleared before the sweep)
+  int32_t* cand_row;     // candidate lists of the exact resolve (see RowResArgs)
+  int32_t* cand_col;
+  int32_t* cand_count;
+  int64_t cand_cap;
   // outputs
   int32_t* count;
   double* best_sim;
@@ -60,8 +112,8 @@ struct TriArgs {
 int tri_rows(int d);
 // Entries of the column-maximum array per head.
 int64_t tri_part_per_head(int64_t N, int rows);
-// Clear, sweep, then resolve (column maxima, candidate blocks, exact column
-// side, final outputs).  `mark` (may be null) is recorded between the sweep
+// Clear, sweep, then resolve (queued rows, column maxima, candidate blocks,
+// exact column side, final outputs).  `mark` (may be null) is recorded between the sweep
 // and the resolve kernels.
 hipError_t launch_tri(const TriArgs& a, hipStream_t stream, hipEvent_t mark);
 
@@ -96,7 +148,7 @@ hipError_t launch_compact(const uint8_t* keep_in, int64_t G, int64_t N, int32_t*
 // whose unrestricted best twin is retained or absent take it as b_i(S0).
 hipError_t launch_rows(const uint8_t* keep_in, const double* prior_sim, const int32_t* prior_idx, int64_t G,
                        int64_t N, int32_t* row_pos, int32_t* nrows, double* best_sim, int32_t* best_idx,
-                       hipStream_t stream);
+                       int32_t* qcount, hipStream_t stream);
 // Copy the retained keys and their inverse norms into column order.
 hipError_t launch_gather(const uint16_t* keys, const float* rinv, const int32_t* pos, const int32_t* ncols, int64_t G,
                          int64_t N, int d, uint16_t* ckeys, float* crinv, hipStream_t stream);

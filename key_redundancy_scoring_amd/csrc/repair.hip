@@ -51,12 +51,14 @@ __global__ __launch_bounds__(kBT) void compact_kernel(const uint8_t* __restrict_
 // S0 has none either.  Those rows take the prior and are not swept; the
 // others are listed in ascending order.  Without a prior every row is
 // listed.  A prior index outside [0, N) other than -1 is treated as not
-// retained, so its row is swept.
+// retained, so its row is swept.  The head's count of rows queued for the
+// exact resolve is zeroed here, before the sweep that fills the queue.
 __global__ __launch_bounds__(kBT) void rows_kernel(const uint8_t* __restrict__ keep_in,
                                                    const double* __restrict__ prior_sim,
                                                    const int32_t* __restrict__ prior_idx, int64_t N,
                                                    int32_t* __restrict__ row_pos, int32_t* __restrict__ nrows,
-                                                   double* __restrict__ best_sim, int32_t* __restrict__ best_idx) {
+                                                   double* __restrict__ best_sim, int32_t* __restrict__ best_idx,
+                                                   int32_t* __restrict__ qcount) {
   __shared__ ScanSmem sc;
   const int64_t g = blockIdx.x;
   const size_t o = (size_t)g * N;
@@ -77,7 +79,10 @@ __global__ __launch_bounds__(kBT) void rows_kernel(const uint8_t* __restrict__ k
     if (f) row_pos[o + base + r] = (int32_t)i;
     base += tot;
   }
-  if (threadIdx.x == 0) nrows[g] = base;
+  if (threadIdx.x == 0) {
+    nrows[g] = base;
+    qcount[g] = 0;
+  }
 }
 
 // Copy retained key rows (and their inverse norms) into column order, so the
@@ -216,9 +221,9 @@ hipError_t launch_compact(const uint8_t* keep_in, int64_t G, int64_t N, int32_t*
 
 hipError_t launch_rows(const uint8_t* keep_in, const double* prior_sim, const int32_t* prior_idx, int64_t G,
                        int64_t N, int32_t* row_pos, int32_t* nrows, double* best_sim, int32_t* best_idx,
-                       hipStream_t stream) {
+                       int32_t* qcount, hipStream_t stream) {
   hipLaunchKernelGGL(rows_kernel, dim3((unsigned)G), dim3(kBT), 0, stream, keep_in, prior_sim, prior_idx, N, row_pos,
-                     nrows, best_sim, best_idx);
+                     nrows, best_sim, best_idx, qcount);
   return hipGetLastError();
 }
 

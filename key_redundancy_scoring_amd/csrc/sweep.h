@@ -79,6 +79,19 @@ __device__ __forceinline__ double dot8_exact(uint4 a, uint4 b) {
   return s;
 }
 
+// (exact cosine, position) -> one 64-bit key whose unsigned order is the
+// cosine's, then the lower position; 0 is below every key.  The low bits
+// selected by idx_mask (2^b - 1 with 2^b >= N) carry idx_mask - position in
+// place of the cosine's lowest mantissa bits, so two cosines that differ only
+// there (by less than 2^(b-52) relative) rank as equal and the lower position
+// wins.
+__device__ __forceinline__ uint64_t pack_best(double sim, int idx, uint64_t idx_mask) {
+  uint64_t u = (uint64_t)__double_as_longlong(sim + 0.0);
+  u = (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+  return (u & ~idx_mask) | (idx_mask - (uint64_t)idx);
+}
+__device__ __forceinline__ int unpack_idx(uint64_t u, uint64_t idx_mask) { return (int)(idx_mask - (u & idx_mask)); }
+
 // XOR swizzle of the 16-byte chunks of stage column c (CH chunks per key).
 // Chunk k of column c lives at slot c*CH + (k ^ swz(c)).  For the A-operand
 // reads (lane l reads chunk k of column l mod 32) this puts any 8 consecutive

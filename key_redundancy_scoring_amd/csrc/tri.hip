@@ -23,7 +23,9 @@
 // blocks whose maximum is within a margin of it, and re-sweep each such
 // block against just those positions to find the exact fp64 best twin.  The
 // row side's own best is made exact at the end of the sweep (the fused
-// fixup).  Both sides merge through a 64-bit atomic maximum of (exact
+// fixup) over the first tile attaining each half-row's maximum; a row where
+// another tile comes within twice the fp32 error of that maximum is queued
+// for the exact resolve of resolve.hip instead.  Both sides merge through a 64-bit atomic maximum of (exact
 // cosine, position) in which the low 30 bits of the order-preserving image
 // of the cosine carry the position, so equal cosines go to the lowest
 // position.  A workgroup sweeps two row blocks, rb and nb-1-rb, so every
@@ -45,10 +47,14 @@ constexpr unsigned kDppMirror = 0x140;      // lane i of a 16-lane row reads lan
 constexpr unsigned kDppHalfMirror = 0x141;  // lane i of an 8-lane half row reads lane 7 - i
 constexpr unsigned kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr unsigned kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
-constexpr uint64_t kIdxMask = (1ull << 30) - 1;
 // screening margin in cosine units: far above the fp32 error of a dot product
 // of at most 128 exact bf16 products scaled by fp32 inverse norms (below 1e-5)
 constexpr float kMargin = 8e-5f;
+// A tile whose fp32 maximum stays more than this (cosine units) below the
+// row's cannot hold the exact best: it exceeds twice the fp32 error of one
+// candidate (below 7.7e-6 at d = 128).  Rows where another tile comes closer
+// go to the exact resolve.
+constexpr float kTieMargin = 2e-5f;
 
 template <unsigned CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -99,14 +105,6 @@ __device__ __forceinline__ int ordered_f32(float v) {
   return b >= 0 ? b : b ^ 0x7FFFFFFF;
 }
 __device__ __forceinline__ float unordered_f32(int o) { return __int_as_float(o >= 0 ? o : o ^ 0x7FFFFFFF); }
-
-// (exact cosine, position) -> one 64-bit key whose unsigned order is the
-// cosine's, then the lower position; 0 is below every key
-__device__ __forceinline__ uint64_t pack_best(double sim, int idx) {
-  uint64_t u = (uint64_t)__double_as_longlong(sim + 0.0);
-  u = (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-  return (u & ~kIdxMask) | (kIdxMask - (uint64_t)idx);
-}
 
 __device__ __forceinline__ int64_t part_offset(int64_t g, int64_t rb, int64_t N, int64_t nb, int rows) {
   const int64_t per_head = nb * N - (int64_t)rows * nb * (nb - 1) / 2;
@@ -260,7 +258,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
     // ---- row keys (rows past the end repeat the last row: their values
     // duplicate a real row's, so column maxima are unaffected; they count nothing)
     bf16x8 brow[RB][KS];
-    float thr[RB], best[RB], rinvr[RB];
+    float thr[RB], best[RB], second[RB], rinvr[RB];  // second: the largest maximum of the other tiles
     int btile[RB], cnt[RB];
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
@@ -276,6 +274,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
                       : (ni == 0.0 && a.tau < 0.0) ? -__builtin_inff() : (float)(a.tau * sqrt(ni)) + 0.0f;
       rinvr[b] = rinv_g[i];
       best[b] = -__builtin_inff();
+      second[b] = -__builtin_inff();
       btile[b] = -1;
       cnt[b] = 0;
     }
@@ -359,6 +358,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
         colmax[r] = (b == 0) ? z : __builtin_fmaxf(colmax[r], z);
       }
       if (live) {  // wave-uniform
+        second[b] = __builtin_amdgcn_fmed3f(m, best[b], second[b]);  // second <= best: max(second, min(m, best))
         btile[b] = m > best[b] ? tile : btile[b];
         best[b] = __builtin_fmaxf(best[b], m);
         if (__ballot(m > thr[b]) != 0ull) count16(acc, b, c0);
@@ -426,6 +426,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
       }
       cnt[b] += twins;
       const float m = max16(yy);
+      second[b] = __builtin_amdgcn_fmed3f(m, best[b], second[b]);
       btile[b] = m > best[b] ? tile : btile[b];
       best[b] = __builtin_fmaxf(best[b], m);
     };
@@ -556,11 +557,24 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
       }
       const int c = cnt[b] + __shfl_xor(cnt[b], 32);
       const float ymax = __builtin_fmaxf(best[b], __shfl_xor(best[b], 32));
+      // another tile of either half within twice the fp32 error of the
+      // row's maximum may hold the exact best: queue the row for the exact
+      // resolve, with candidates down to the screening margin below the
+      // maximum.  A zero key is settled here: all its cosines are exactly 0
+      // and the first tile holds the lowest eligible position.
+      const bool near = second[b] >= ymax - kTieMargin * (float)sqrt(ni);
+      const bool near_o = __shfl_xor((int)near, 32) != 0;  // both lanes of the row take part in the shuffle
+      const bool amb = row_ok && ni > 0.0 && ymax > -__builtin_inff() && (near || near_o);
       if (h == 0 && row_ok) {
         const size_t o = (size_t)g * N + i;
-        a.best64[o] = aa >= 0 ? pack_best(bb, aa) : 0ull;
+        a.best64[o] = aa >= 0 ? pack_best(bb, aa, a.idx_mask) : 0ull;
         a.rowcos[o] = ymax > -__builtin_inff() ? ymax * rinvr[b] : -__builtin_inff();
         a.rcount[o] = c;
+        if (amb) {
+          const int k = atomicAdd(&a.q.count[g], 1);
+          a.q.row[(size_t)g * N + k] = i;
+          a.q.thr[(size_t)g * N + k] = ymax * rinvr[b] - kMargin;
+        }
       }
     }
     __syncthreads();  // LDS is reused by the next pass
@@ -799,7 +813,7 @@ __global__ __launch_bounds__(256, S::D == 64 ? 2 : 1) void tri_colres_kernel(Tri
       }
     }
     if (h == 0 && ok && aa >= 0)
-      atomicMax((unsigned long long*)&a.best64[(size_t)g * N + k], (unsigned long long)pack_best(bb, aa));
+      atomicMax((unsigned long long*)&a.best64[(size_t)g * N + k], (unsigned long long)pack_best(bb, aa, a.idx_mask));
   };
 
 #pragma unroll 1
@@ -864,7 +878,7 @@ __global__ __launch_bounds__(256) void tri_finalize_kernel(TriArgs a) {
   double bb = -1.0;
   int aa = -1;
   if (u != 0ull) {
-    aa = (int)(kIdxMask - (u & kIdxMask));
+    aa = unpack_idx(u, a.idx_mask);
     const uint4* ki = reinterpret_cast<const uint4*>(a.keys) + (size_t)q * CH;
     const uint4* kj = reinterpret_cast<const uint4*>(a.keys) + ((size_t)g * N + aa) * CH;
     double dot = 0.0;
@@ -882,10 +896,12 @@ __global__ __launch_bounds__(256) void tri_finalize_kernel(TriArgs a) {
   if (a.omega) a.omega[q] = disc / log((double)(N + 1));
 }
 
-__global__ __launch_bounds__(256) void tri_clear_kernel(int32_t* ccount, int64_t n, uint32_t* cbits, int64_t nbits) {
+__global__ __launch_bounds__(256) void tri_clear_kernel(int32_t* ccount, int64_t n, uint32_t* cbits, int64_t nbits,
+                                                        int32_t* qcount, int64_t G) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n; q += stride) ccount[q] = 0;
   for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < nbits; q += stride) cbits[q] = 0u;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < G; q += stride) qcount[q] = 0;
 }
 
 template <class S>
@@ -894,12 +910,32 @@ hipError_t launch_d(const TriArgs& a, hipStream_t stream, hipEvent_t mark) {
   const int64_t nbits = a.G * a.nb * a.words;
   int64_t cb = (n > nbits ? n : nbits) / 256 + 1;
   cb = cb < 8192 ? cb : 8192;
-  hipLaunchKernelGGL(tri_clear_kernel, dim3((unsigned)cb), dim3(256), 0, stream, a.ccount, n, a.cbits, nbits);
   const int64_t total = a.G * ((a.nb + 1) / 2);
   const int64_t grid = 8 * ((total + 7) / 8);
   if (grid > INT_MAX || a.G * a.nb > INT_MAX || (n + 255) / 256 > INT_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tri_clear_kernel, dim3((unsigned)cb), dim3(256), 0, stream, a.ccount, n, a.cbits, nbits,
+                     a.q.count, a.G);
   hipLaunchKernelGGL((tri_sweep_kernel<S>), dim3((unsigned)grid), dim3(64 * S::WAVES), 0, stream, a);
   if (mark && hipEventRecord(mark, stream) != hipSuccess) return hipErrorInvalidValue;
+  RowResArgs r{};
+  r.keys = a.keys;
+  r.nsq = a.nsq;
+  r.rinv = a.rinv;
+  r.col_keys = a.keys;
+  r.col_rinv = a.rinv;
+  r.q = a.q;
+  r.G = a.G;
+  r.N = a.N;
+  r.d = a.d;
+  r.window = a.window;
+  r.best64 = a.best64;
+  r.idx_mask = a.idx_mask;
+  r.cand_row = a.cand_row;
+  r.cand_col = a.cand_col;
+  r.cand_count = a.cand_count;
+  r.cand_cap = a.cand_cap;
+  const hipError_t e = launch_rowres(r, stream);
+  if (e != hipSuccess) return e;
   const unsigned kb = (unsigned)((n + 255) / 256);
   hipLaunchKernelGGL((tri_colmax_kernel<S::ROWS>), dim3(kb), dim3(256), 0, stream, a);
   hipLaunchKernelGGL((tri_colres_kernel<S>), dim3((unsigned)(a.G * a.nb)), dim3(256), 0, stream, a);

@@ -11,25 +11,27 @@ workloads).
 * tau band: a pair with |sim - tau| < 1e-3 may fall on either side of tau in
   fp32; the GPU count must lie in [c_lo, c_lo + band], where c_lo counts the
   nonlocal pairs with sim >= tau + 1e-3 and band counts those inside the band.
-* argmax near-ties: the sweep's fp32 value of a candidate is within 1e-5 of
-  its exact cosine (relative to ||k_i||: at most d fp32 roundings of sums of
-  exact bf16 products, one of 1/||k_j|| and one of the product, about
-  8e-6 at d = 128).  Two candidates less than twice that apart may swap
-  order, so a row with an eligible similarity strictly below its maximum by
-  less than NEAR_TIE = 2e-5 may legitimately pick that position.  Such a row is
-  not skipped: when the GPU's position differs from the oracle's, the test
-  checks that it is an eligible position whose exact cosine lies within
-  NEAR_TIE of (and strictly below) the oracle's maximum, and that the GPU
-  reports that cosine.  Exact ties with the maximum must resolve to the
-  lowest position.
+* argmax near-ties: both sweeps settle every candidate within twice the fp32
+  error of a row's maximum in fp64 (a row where another tile comes that
+  close goes to the exact resolve), so the GPU's best twin is the exact
+  maximum at its lowest position, up to two limits: the two sides' fp64
+  cosines of one pair agree to EXACT_SIM_RTOL, and the score pass merges its
+  row and column sides through a 64-bit key that keeps the cosine's bits
+  above the lowest ceil(log2 N) (2^-34 relative at N <= 2^18).  A row where
+  the GPU's position differs from the oracle's must therefore be a near-tie
+  whose pick lies within TIE_RTOL of the maximum (strictly below it: exact
+  ties resolve to the lowest position), and the GPU must report the pick's
+  exact cosine.  Rows with an eligible similarity strictly below the
+  maximum by less than NEAR_TIE = 2e-5 are counted as near-tie rows (the
+  stored oracle results list their candidates).
 * selection: heads with a band-affected row, or whose kept/evicted boundary
   ranks differ by a relative score gap below 1e-12, are checked by the
   properties a top-k selection must have instead of bit for bit (the oracle
   never takes a GPU value as input).
 * repair: when a row's best surviving twin differs at a validated near-tie,
-  |O|, |D| and m are still compared exactly unless that row's b lies within
-  2 * NEAR_TIE of tau; S1 and the swap pairs are compared exactly unless such
-  a row is an orphan or donor (its rank may then move).
+  the swap rule decides exactly whether that changes |O|, |D|, m, the pairs
+  or S1 (it is applied to the GPU's b and to the GPU's b with the oracle's
+  maxima put back); if not, they are compared bit for bit.
 """
 from __future__ import annotations
 
@@ -38,8 +40,11 @@ import numpy as np
 from oracle import twinkv_oracle as O
 
 BAND = 1e-3
-# twice the sweep's per-candidate error bound of 1e-5 (see above)
+# near-tie rows, counted and listed (see above)
 NEAR_TIE = 2e-5
+# how far below the oracle's maximum a differing pick may lie, relative: the
+# packed merge of the score pass (2^-34 at N <= 2^18) or fp64 rounding
+TIE_RTOL = 2.0 ** -34
 BOUNDARY_GAP = 1e-12
 # Energies and squared norms are fp64 sums of d exact products (bf16 squares
 # are exact).  Both sides add the same non-negative terms in different orders,
@@ -70,20 +75,17 @@ class Tally:
             if sub in rep:
                 self.add(rep[sub])
 
-    def check(self, near_tie_frac: float = 1e-3, **bounds):
+    def check(self, near_tie_frac: float = 1e-6, **bounds):
         """Print the totals; assert every bounded kind (default bound 0 for
-        band rows and inexact selections; 2% of the repaired heads, at least
-        one, for heads whose swap a validated near-tie pick changes) and the
-        fraction of rows whose argmax took the other side of a validated
-        near-tie."""
+        band rows, inexact selections and swaps changed by a near-tie pick)
+        and the fraction of rows whose argmax took another candidate within
+        TIE_RTOL of the maximum."""
         print(f"[{self.tag}] exclusions: {self.c}", flush=True)
-        affected = max(1, -(-2 * self.c["repair_heads"] // 100))
-        lim = {"band_rows": 0, "select_inexact_heads": 0, "repair_class_ambiguous": affected,
-               "repair_rank_affected": affected}
+        lim = {"band_rows": 0, "select_inexact_heads": 0, "repair_class_ambiguous": 0, "repair_rank_affected": 0}
         lim.update(bounds)
         for k, v in lim.items():
             assert self.c[k] <= v, f"{self.tag}: {self.c[k]} {k} (bound {v}); all counts {self.c}"
-        assert self.c["near_tie_differs"] <= near_tie_frac * max(1, self.c["rows"]), \
+        assert self.c["near_tie_differs"] <= max(1.0, near_tie_frac * self.c["rows"]), \
             f"{self.tag}: {self.c['near_tie_differs']} near-tie argmax picks differ over {self.c['rows']} rows"
         return self.c
 
@@ -146,7 +148,9 @@ def validate_near_tie_picks(ref, rows, ga, gb, allowed=None, tag=""):
         if allowed is not None:
             assert allowed[j] != 0, f"{tag} row {i}: near-tie pick {j} is not retained"
         sim = float(O.cosine_rows(K, n, np.array([i]), np.array([j]))[0, 0])
-        assert sim >= ref["best"][t] - NEAR_TIE, f"{tag} row {i}: pick {j} at {sim} vs max {ref['best'][t]}"
+        top = float(ref["best"][t])
+        tol = max(TIE_RTOL, 2 * EXACT_SIM_RTOL) * max(abs(top), 1e-300)
+        assert sim >= top - tol, f"{tag} row {i}: pick {j} at {sim} is not the maximum {top} (tolerance {tol:.3g})"
         # an exact tie with the maximum must go to the lowest position, the oracle's
         assert sim < ref["best"][t], f"{tag} row {i}: pick {j} ties the maximum but is not the lowest position"
         assert abs(gb[t] - sim) <= EXACT_SIM_RTOL * abs(sim), f"{tag} row {i}: reported {gb[t]} for {sim}"

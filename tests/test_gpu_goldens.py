@@ -79,9 +79,10 @@ def _pairs_sim(K, n, rows, cols):
 
 def _check_picks(gpu_arg, near, K, n, best_sim_gpu, tag, allowed=None):
     """Near-tie rows: the GPU's pick is a stored candidate (eligible and within
-    NEAR_TIE of the maximum), and not an exact tie of the maximum other than
-    the lowest position.  Returns the arg array with those rows masked and the
-    oracle's maximum at each row whose pick differs from the oracle's."""
+    NEAR_TIE of the maximum), within TIE_RTOL of the maximum, and not an
+    exact tie of the maximum other than the lowest position.  Returns the arg
+    array with those rows masked and the oracle's maximum at each row whose
+    pick differs from the oracle's."""
     masked = gpu_arg.astype(np.int64).copy()
     differs = {}
     for key, cand in near.items():
@@ -96,6 +97,8 @@ def _check_picks(gpu_arg, near, K, n, best_sim_gpu, tag, allowed=None):
         lowest_top = min(c for c, s in zip(cand, sims) if s == top)
         pick_sim = sims[cand.index(j)]
         assert pick_sim < top or j == lowest_top, f"{tag} row {r}: pick {j} ties the maximum but is not the lowest"
+        tol = max(PR.TIE_RTOL, 2 * PR.EXACT_SIM_RTOL) * max(abs(top), 1e-300)
+        assert pick_sim >= top - tol, f"{tag} row {r}: pick {j} at {pick_sim} is not the maximum {top}"
         assert abs(best_sim_gpu[r] - pick_sim) <= PR.EXACT_SIM_RTOL * abs(pick_sim), f"{tag} row {r}: reported sim"
         if j != lowest_top:  # the oracle's pick: the lowest position attaining the maximum
             differs[r] = float(top)

@@ -342,3 +342,69 @@ def test_repair_prior_out_of_range_indices_are_swept():
     fa, pa = full["best_idx"].cpu().numpy(), pr["best_idx"].cpu().numpy()
     np.testing.assert_array_equal(pa[rows], fa[rows])
     np.testing.assert_array_equal(pr["best_sim"].cpu().numpy()[rows], full["best_sim"].cpu().numpy()[rows])
+
+
+def _plant_near_tie(rng, d, lo=1e-9, hi=3e-6):
+    """A row key and two candidate keys whose exact cosines with it differ by
+    lo < gap < hi, below the fp32 error of the sweep: the second candidate is
+    the first with one small bf16 component moved by one unit in the last
+    place.  Returns bf16 bits (row, first, second) and the two cosines."""
+    while True:
+        base = rng.standard_normal(d)
+        row = _bf16(base + 0.05 * rng.standard_normal(d))
+        a = _bf16(base)
+        r64 = O.widen_bf16(row)
+        for c in np.argsort(np.abs(O.widen_bf16(a)))[:16]:
+            b = a.copy()
+            b[c] = np.uint16(int(b[c]) + 1)
+            K = O.widen_bf16(np.stack([row, a, b]))
+            n = O.squared_norms(K)
+            s = O.cosine_rows(K, n, np.array([0]), np.array([1, 2]))[0]
+            if lo < abs(s[1] - s[0]) < hi:
+                return row, a, b, s
+
+
+def test_cross_tile_near_ties_resolve_exactly():
+    """Rows whose two best candidates sit in different tiles of the same
+    half-row (positions = 0 mod 8) with exact cosines closer than the fp32
+    error: the score pass and the repair sweep must both return the exact
+    maximum.  Planted on both sides of the row (later columns: the row side
+    of the single-order sweep; earlier ones: its column side)."""
+    rng = np.random.default_rng(77)
+    N, d, w = 1600, 64, 8
+    K = _bf16(rng.standard_normal((N, d)))
+    planted = {}
+    for k in range(12):
+        row, a, b, s = _plant_near_tie(rng, d)
+        if k % 2:  # the larger cosine at the earlier position half of the time
+            a, b, s = b, a, s[::-1]
+        if k < 6:  # candidates after the row
+            i, j1, j2 = 40 + k, 296 + 40 * k, 704 + 48 * k
+        else:      # candidates before the row
+            i, j1, j2 = 1500 + k, 96 + 24 * (k - 6), 520 + 40 * (k - 6)
+        K[i], K[j1], K[j2] = row, a, b
+        planted[i] = j1 if s[0] > s[1] else j2
+    V = _bf16(rng.standard_normal((N, d)))
+    _say("[cross-tile near-ties]")
+    res = _score_one(K[None], V[None], 0.9, w)
+    ref = PR.score_reference(K, V, 0.9, w)
+    got = res["best_idx"][0].cpu().numpy()
+    for i, j in planted.items():
+        assert ref["arg"][i] == j, f"planted row {i}: oracle picks {ref['arg'][i]}, expected {j}"
+        assert got[i] == j, f"score pass, row {i}: picks {got[i]}, exact best {j}"
+    tally = PR.Tally("cross-tile near-ties")
+    tally.add(PR.compare_score(_score_numpy(res, 0), ref, tag="cross-tile score"))
+    # the repair sweep over every retained column but a few, without a prior
+    keep = np.ones((1, N), np.uint8)
+    keep[0, 1:N:97] = 0
+    rep = krs.repair(_up(K[None]), torch.from_numpy(keep).to(_dev()), 0.9, w, 4, 8)
+    torch.cuda.synchronize()
+    rref = PR.repair_reference(K, keep[0], 0.9, w, 4, 8)
+    rb = rep["best_idx"][0].cpu().numpy()
+    for i in planted:
+        assert rb[i] == rref["arg"][i], f"repair sweep, row {i}: picks {rb[i]}, exact best {rref['arg'][i]}"
+    rg = {k: rep[k][0].cpu().numpy() for k in ("keep", "n_orphans", "n_donors", "n_swaps", "pairs")}
+    rg["best"] = rep["best_sim"][0].cpu().numpy()
+    rg["arg"] = rb
+    tally.add(PR.compare_repair(rg, rref, keep[0], 0.9, tag="cross-tile repair"))
+    tally.check()
