@@ -136,13 +136,17 @@ const char* twinkv_status_string(int status);
  * keys, values: bf16 [G][N][d].  count, best_idx: int32 [G][N].
  * best_sim, energy, score, omega: double [G][N].
  * Each unordered nonlocal pair is evaluated once (on the MFMA matrix cores,
- * bf16 products exact, fp32 sums); the chosen best twin is then recomputed
- * in fp64.  The workspace grows with N: about 48 bytes per key plus
- * 2 bytes * N / 384 (d = 64) or N / 256 (d = 128) per key for the column
- * maxima of each row block.
+ * bf16 products exact, fp32 sums); every candidate within the fp32 error of
+ * a position's maximum is then evaluated in fp64, so best_idx is the exact
+ * argmax of the fp64 cosines at its lowest position, except that cosines
+ * closer than 2^(b-52) relative (b = ceil(log2 N)) rank as equal and the
+ * lower position wins.  The workspace grows with N: about 52 bytes per key
+ * plus 2N/R + N/(8R) bytes per key (R = 384 rows per block at d = 64, 256
+ * at d = 128) for the column maxima and candidate bits of each row block.
  * Phases for `marks`: 0 = norms and energies, 1 = single-order Gram sweep
- * (counts, row-side best twin, column maxima), 2 = resolve (exact column-side
- * best twin, outputs and scores).
+ * (counts, row-side best twin, column maxima), 2 = resolve (exact best twin
+ * of the rows two tiles nearly tie, exact column-side best twin, outputs and
+ * scores).
  */
 int twinkv_score(const twinkv_params* params, const void* keys, const void* values,
                  int32_t* count, double* best_sim, int32_t* best_idx, double* energy,
@@ -214,7 +218,8 @@ int twinkv_capacity_offsets(const int32_t* capacity, int64_t G, int64_t N, int64
  * of every head at its own budget K = |S0| ([P1] section 3.4):
  *   best_sim[g][i] = b_i(S0) = max over j in S0, |i-j| > window of sim(i,j), or -1
  *                    (exact fp64 for the chosen j)                       ([P1] Eq. 4)
- *   best_idx[g][i] = the lowest such j attaining it, or -1
+ *   best_idx[g][i] = the lowest such j attaining it, or -1 (every candidate
+ *                    within the fp32 error of the maximum is evaluated in fp64)
  *   orphans  O = { i not in S0 : b_i < tau } ranked by (b asc, i asc)
  *   donors   D = { j in S0 outside the protected regions : b_j >= tau } ranked by
  *              (b desc, j asc); the protected regions are the first
@@ -231,15 +236,14 @@ int twinkv_capacity_offsets(const int32_t* capacity, int64_t G, int64_t N, int64
  *   no nonlocal position exists), it is b_i(S0) with its position, since the
  *   lowest position attaining the maximum over all nonlocal j is then in S0;
  *   those rows are copied and only the others are swept.  The outputs are the
- *   same as without a prior, except that such a row reports the prior's
- *   (exact fp64) choice where two positions' fp32 similarities are within
- *   rounding of each other.  An index outside [0, N) other than -1 counts as
+ *   same as without a prior.  An index outside [0, N) other than -1 counts as
  *   not retained (that row is swept); any other inconsistent prior gives wrong
  *   results, never an access outside the stated sizes.  Both NULL: every row
  *   is swept.
  * Phases for `marks`: 0 = norms, 1 = compaction of S0 (retained positions and a
  * contiguous copy of their keys) and of the rows to sweep, 2 = restricted
- * Gram and fixup, 3 = classification, ranking and swap.
+ * Gram, fixup and exact resolve of near-tied rows, 3 = classification, ranking
+ * and swap.
  */
 int twinkv_repair(const twinkv_params* params, const void* keys, const uint8_t* keep_in,
                   const double* prior_sim, const int32_t* prior_idx, uint8_t* keep_out,
