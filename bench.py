@@ -165,16 +165,24 @@ def cpu_baseline(cfg, overrides: dict, capacities, cores: int | None = None):
 
 def calibrate_copy():
     """A plain device-to-device copy of 1 GiB, five times, for scaling the
-    FETCH_SIZE / WRITE_SIZE counters."""
+    FETCH_SIZE / WRITE_SIZE counters; the same copies timed (bytes read plus
+    written per second: the practical ceiling of a streaming kernel)."""
     import torch
 
     n = 1 << 30
     a = torch.ones(n, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
-    for _ in range(5):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    ev[0].record()
+    for k in range(5):
         b.copy_(a)
+        ev[k + 1].record()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_per_launch": n}), flush=True)
+    ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(5)]
+    best = min(ms[1:])  # the first copy also pages in
+    print(json.dumps({"copy_bytes_per_launch": n, "copy_ms": ms,
+                      "copy_GBs": 2 * n / (best * 1e-3) / 1e9,
+                      "copy_frac_hbm": 2 * n / (best * 1e-3) / 1e9 / PEAK_HBM_GBS}), flush=True)
 
 
 def _upload_heads(cfg, torch, dev):

@@ -20,6 +20,14 @@ namespace {
 constexpr int kGT = 256;  // threads per block
 constexpr int kPasses = 4;
 
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p)));
+}
+__device__ __forceinline__ void store_nt(uint4* p, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u4v, v), reinterpret_cast<u4v*>(p));
+}
+
 template <int CH>
 __global__ __launch_bounds__(kGT) void gather_kv_kernel(const uint4* __restrict__ keys, const uint4* __restrict__ values,
                                                         const int32_t* __restrict__ kept_idx,
@@ -39,16 +47,33 @@ __global__ __launch_bounds__(kGT) void gather_kv_kernel(const uint4* __restrict_
   const int64_t r0 = x * RPB;
   if (r0 >= cnt) return;
   const int c = threadIdx.x % CH;
+  // the indices, then every row's loads, then the stores: 2 * kPasses
+  // 16-byte loads in flight per lane; source and destination are touched
+  // once, so loads and stores are nontemporal
+  int64_t src[kPasses];
+  bool ok[kPasses];
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const int64_t row = r0 + p * RPP + threadIdx.x / CH;
-    if (row < cnt) {
-      int64_t i = kept_idx[o0 + row];
-      i = i < 0 ? 0 : (i >= N ? N - 1 : i);
-      const int64_t src = (g * N + i) * CH + c;
-      const int64_t dst = (o0 + row) * CH + c;
-      out_keys[dst] = keys[src];
-      if (values) out_values[dst] = values[src];
+    ok[p] = row < cnt;
+    int64_t i = ok[p] ? kept_idx[o0 + row] : 0;
+    i = i < 0 ? 0 : (i >= N ? N - 1 : i);
+    src[p] = (g * N + i) * CH + c;
+  }
+  uint4 kv[kPasses], vv[kPasses];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    if (ok[p]) {
+      kv[p] = load_nt(keys + src[p]);
+      if (values) vv[p] = load_nt(values + src[p]);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    if (ok[p]) {
+      const int64_t dst = (o0 + r0 + p * RPP + threadIdx.x / CH) * CH + c;
+      store_nt(out_keys + dst, kv[p]);
+      if (values) store_nt(out_values + dst, vv[p]);
     }
   }
 }

@@ -39,28 +39,50 @@ __device__ __forceinline__ double group_sum(double v) {
   return v;
 }
 
+// Each LPK-lane group takes kRows consecutive key rows per step and issues
+// all their loads, keys and values, before the first sum: 2 * kRows 16-byte
+// loads in flight per lane.  Lane u of the group then writes row u's
+// results, so a wave's stores cover consecutive keys.  Keys and values are
+// read once here, so the loads are nontemporal.
+constexpr int kRows = 4;
+
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  typedef unsigned u4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u4*>(p)));
+}
+
 template <int D, bool WITH_V>
 __global__ __launch_bounds__(256) void norms_energy_kernel(const uint4* __restrict__ K, const uint4* __restrict__ V,
                                                            int64_t nkeys, double* __restrict__ nsq,
                                                            float* __restrict__ rinv, double* __restrict__ energy) {
-  constexpr int LPK = D / 8;         // lanes per key row
-  constexpr int KPB = 256 / LPK;     // key rows per block per step
+  constexpr int LPK = D / 8;           // lanes per key row
+  constexpr int GPB = 256 / LPK;       // lane groups per block
+  static_assert(kRows <= LPK, "one writing lane per row of the group");
   const int sub = threadIdx.x % LPK;
-  const int64_t stride = (int64_t)gridDim.x * KPB;
-  for (int64_t key = (int64_t)blockIdx.x * KPB + threadIdx.x / LPK; key < nkeys; key += stride) {
+  const int64_t stride = (int64_t)gridDim.x * GPB * kRows;
+  for (int64_t key0 = ((int64_t)blockIdx.x * GPB + threadIdx.x / LPK) * kRows; key0 < nkeys; key0 += stride) {
     // a whole LPK-lane group is either inside or outside the range, so the
     // group-wide shuffles below always see active partners
-    const uint4 kv = K[key * LPK + sub];
-    double n = group_sum<LPK>(sumsq8(kv));
-    double e = 0.0;
-    if (WITH_V) {
-      const uint4 vv = V[key * LPK + sub];
-      e = group_sum<LPK>(sumsq8(vv));
+    uint4 kv[kRows], vv[kRows];
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const int64_t key = key0 + u;
+      kv[u] = key < nkeys ? load_nt(K + key * LPK + sub) : make_uint4(0u, 0u, 0u, 0u);
+      if (WITH_V) vv[u] = key < nkeys ? load_nt(V + key * LPK + sub) : make_uint4(0u, 0u, 0u, 0u);
     }
-    if (sub == 0) {
-      nsq[key] = n;
-      rinv[key] = n > 0.0 ? (float)(1.0 / sqrt(n)) : 0.0f;
-      if (WITH_V) energy[key] = e;
+    double n_mine = 0.0, e_mine = 0.0;
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const double n = group_sum<LPK>(sumsq8(kv[u]));
+      const double e = WITH_V ? group_sum<LPK>(sumsq8(vv[u])) : 0.0;
+      n_mine = sub == u ? n : n_mine;
+      e_mine = sub == u ? e : e_mine;
+    }
+    const int64_t key = key0 + sub;
+    if (sub < kRows && key < nkeys) {
+      nsq[key] = n_mine;
+      rinv[key] = n_mine > 0.0 ? (float)(1.0 / sqrt(n_mine)) : 0.0f;
+      if (WITH_V) energy[key] = e_mine;
     }
   }
 }
@@ -68,9 +90,9 @@ __global__ __launch_bounds__(256) void norms_energy_kernel(const uint4* __restri
 template <int D>
 hipError_t launch_d(const uint16_t* keys, const uint16_t* values, int64_t nkeys, double* nsq, float* rinv,
                     double* energy, hipStream_t stream) {
-  constexpr int KPB = 256 / (D / 8);
+  constexpr int KPB = 256 / (D / 8) * kRows;  // keys per block per step
   int64_t blocks = (nkeys + KPB - 1) / KPB;
-  if (blocks > 256 * 64) blocks = 256 * 64;
+  if (blocks > (1 << 20)) blocks = 1 << 20;  // a grid-stride loop covers the rest
   if (blocks < 1) blocks = 1;
   if (values)
     hipLaunchKernelGGL((norms_energy_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
