@@ -568,6 +568,8 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
       if (h == 0 && row_ok) {
         const size_t o = (size_t)g * N + i;
         a.best64[o] = aa >= 0 ? pack_best(bb, aa, a.idx_mask) : 0ull;
+        a.best_sim[o] = bb;  // the row side's exact result, kept for the finalize
+        a.best_idx[o] = aa;
         a.rowcos[o] = ymax > -__builtin_inff() ? ymax * rinvr[b] : -__builtin_inff();
         a.rcount[o] = c;
         if (amb) {
@@ -877,7 +879,13 @@ __global__ __launch_bounds__(256) void tri_finalize_kernel(TriArgs a) {
   const uint64_t u = a.best64[q];
   double bb = -1.0;
   int aa = -1;
-  if (u != 0ull) {
+  // the sweep's fixup left its own exact result in best_sim / best_idx: when
+  // the packed best still names that position, its cosine is already exact
+  const int aa_row = a.best_idx[q];
+  if (u != 0ull && unpack_idx(u, a.idx_mask) == aa_row) {
+    aa = aa_row;
+    bb = a.best_sim[q];
+  } else if (u != 0ull) {
     aa = unpack_idx(u, a.idx_mask);
     const uint4* ki = reinterpret_cast<const uint4*>(a.keys) + (size_t)q * CH;
     const uint4* kj = reinterpret_cast<const uint4*>(a.keys) + ((size_t)g * N + aa) * CH;
