@@ -408,3 +408,27 @@ def test_cross_tile_near_ties_resolve_exactly():
     rg["arg"] = rb
     tally.add(PR.compare_repair(rg, rref, keep[0], 0.9, tag="cross-tile repair"))
     tally.check()
+
+
+def test_all_identical_keys_overflow_the_candidate_lists():
+    """Every key the same: every cosine is exactly 1, every row is queued for
+    the exact resolve and each has far more candidates than its list holds,
+    so the rows go to the exhaustive pass.  The best twin is the lowest
+    eligible position, with cosine 1, in the score pass and in the repair
+    sweep alike."""
+    rng = np.random.default_rng(9)
+    N, d, w = 2100, 64, 16
+    K = np.repeat(_bf16(rng.standard_normal((1, 1, d))), N, axis=1)
+    V = _bf16(rng.standard_normal((1, N, d)))
+    want = np.where(np.arange(N) > w, 0, np.arange(N) + w + 1)  # the lowest j with |i - j| > w
+    _say("[identical keys, overflow]")
+    res = _score_one(K, V, 0.5, w)
+    np.testing.assert_array_equal(res["best_idx"][0].cpu().numpy(), want)
+    assert np.all(res["best_sim"][0].cpu().numpy() == 1.0)
+    keep = np.ones((1, N), np.uint8)
+    keep[0, :5] = 0  # the lowest positions evicted: the answer moves
+    rep = krs.repair(_up(K), torch.from_numpy(keep).to(_dev()), 0.5, w, 4, 8)
+    torch.cuda.synchronize()
+    rref = PR.repair_reference(K[0], keep[0], 0.5, w, 4, 8)
+    np.testing.assert_array_equal(rep["best_idx"][0].cpu().numpy(), rref["arg"])
+    assert np.all(rep["best_sim"][0].cpu().numpy() == 1.0)
