@@ -364,14 +364,15 @@ def _plant_near_tie(rng, d, lo=1e-9, hi=3e-6):
                 return row, a, b, s
 
 
-def test_cross_tile_near_ties_resolve_exactly():
+@pytest.mark.parametrize("d", [64, 128])
+def test_cross_tile_near_ties_resolve_exactly(d):
     """Rows whose two best candidates sit in different tiles of the same
     half-row (positions = 0 mod 8) with exact cosines closer than the fp32
     error: the score pass and the repair sweep must both return the exact
     maximum.  Planted on both sides of the row (later columns: the row side
     of the single-order sweep; earlier ones: its column side)."""
-    rng = np.random.default_rng(77)
-    N, d, w = 1600, 64, 8
+    rng = np.random.default_rng(77 + d)
+    N, w = 1600, 8
     K = _bf16(rng.standard_normal((N, d)))
     planted = {}
     for k in range(12):
@@ -385,7 +386,7 @@ def test_cross_tile_near_ties_resolve_exactly():
         K[i], K[j1], K[j2] = row, a, b
         planted[i] = j1 if s[0] > s[1] else j2
     V = _bf16(rng.standard_normal((N, d)))
-    _say("[cross-tile near-ties]")
+    _say(f"[cross-tile near-ties d={d}]")
     res = _score_one(K[None], V[None], 0.9, w)
     ref = PR.score_reference(K, V, 0.9, w)
     got = res["best_idx"][0].cpu().numpy()
