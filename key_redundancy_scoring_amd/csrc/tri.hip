@@ -43,10 +43,6 @@ namespace {
 using TriShape64 = GramShape<64, 3, 4, 256, 2>;
 using TriShape128 = GramShape<128, 2, 4, 128, 2>;
 
-constexpr unsigned kDppMirror = 0x140;      // lane i of a 16-lane row reads lane 15 - i
-constexpr unsigned kDppHalfMirror = 0x141;  // lane i of an 8-lane half row reads lane 7 - i
-constexpr unsigned kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
-constexpr unsigned kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
 // screening margin in cosine units: far above the fp32 error of a dot product
 // of at most 128 exact bf16 products scaled by fp32 inverse norms (below 1e-5)
 constexpr float kMargin = 8e-5f;
@@ -56,47 +52,54 @@ constexpr float kMargin = 8e-5f;
 // go to the exact resolve.
 constexpr float kTieMargin = 2e-5f;
 
-template <unsigned CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-// The 16 accumulator values of a lane are 16 columns (tile_col(r, h)) for the
-// lane's row; the 32 lanes of a half-wave share those columns.  Returns, in
-// every lane, the maximum over its half-wave of column slot
-// 8*b1 + 4*b2 + 2*b3 + b4 (bk: bit k of the lane id); lanes l and l^1 agree.
-__device__ __forceinline__ float reduce_scatter16(const float (&v)[16]) {
-  const int l = threadIdx.x & 63;
+// Column maxima of a tile over the 32 lanes of each half-wave.  The 16
+// accumulator values of a lane are 16 columns (tile_col(r, h)) of the lane's
+// row; the 32 lanes of a half-wave share those columns.  A swap across the
+// 16-lane rows pairs lanes l and l^16; inside a row, lane p pairs with 15 - p
+// and then with 7 - p (DPP mirrors): of each pair of values the lanes keep
+// one column, and the DPP bank mask (a bank is a group of four lanes of a
+// row) writes each column only into the lanes that keep it, so no lane
+// selects are needed; the last two pairings, inside 4-lane quads, reduce
+// fully.  On return every lane holds the maxima of column slots s and s + 8,
+// s = 4*b2 + 2*b3 + b4 (bk: bit k of the lane id).  The DPP reads follow
+// their inputs' writes by the two wait states the hardware requires.
+__device__ __forceinline__ void reduce_cols(const float (&v)[16], float& c0, float& c1) {
   float a[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    // rows of 16 lanes: odd rows of v[2k] swap with even rows of v[2k+1]
+    // odd rows of v[2k] swap with even rows of v[2k+1]: the even rows then
+    // hold slot 2k of lanes l and l^16, the odd rows slot 2k+1
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[2 * k]), __float_as_uint(v[2 * k + 1]), false, false);
     a[k] = __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
   }
-  const bool b3 = (l >> 3) & 1, b2 = (l >> 2) & 1, b1 = (l >> 1) & 1;
-  float b[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const float keep = b3 ? a[2 * m + 1] : a[2 * m];
-    const float send = b3 ? a[2 * m] : a[2 * m + 1];
-    b[m] = __builtin_fmaxf(keep, dpp<kDppMirror>(send));
-  }
-  float c[2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const float keep = b2 ? b[2 * m + 1] : b[2 * m];
-    const float send = b2 ? b[2 * m] : b[2 * m + 1];
-    c[m] = __builtin_fmaxf(keep, dpp<kDppHalfMirror>(send));
-  }
-  const float keep = b1 ? c[1] : c[0];
-  const float send = b1 ? c[0] : c[1];
-  const float e = __builtin_fmaxf(keep, dpp<kDppXor2>(send));
-  return __builtin_fmaxf(e, dpp<kDppXor1>(e));
-}
-
-__device__ __forceinline__ int slot_of_lane(int lane) {
-  return 8 * ((lane >> 1) & 1) + 4 * ((lane >> 2) & 1) + 2 * ((lane >> 3) & 1) + ((lane >> 4) & 1);
+  float b0, b1, b2, b3;
+  // lanes 0-7 of a row (banks 0, 1) keep a[2m], lanes 8-15 a[2m+1]
+  asm("s_nop 1\n\t"
+      "v_max_f32_dpp %0, %4, %4 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %0, %5, %5 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %1, %6, %6 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %1, %7, %7 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %2, %8, %8 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %2, %9, %9 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %3, %10, %10 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %3, %11, %11 row_mirror row_mask:0xf bank_mask:0xc"
+      : "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
+  // lanes 0-3 and 8-11 (banks 0, 2) keep b[2m], lanes 4-7 and 12-15 b[2m+1];
+  // then each quad reduces both values
+  asm("s_nop 1\n\t"
+      "v_max_f32_dpp %0, %2, %2 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_max_f32_dpp %0, %3, %3 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_max_f32_dpp %1, %4, %4 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_max_f32_dpp %1, %5, %5 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+      : "=&v"(c0), "=&v"(c1)
+      : "v"(b0), "v"(b1), "v"(b2), "v"(b3));
 }
 
 // fp32 <-> int with the same order (for atomic maxima of signed values)
@@ -364,11 +367,19 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
         if (__ballot(m > thr[b]) != 0ull) count16(acc, b, c0);
       }
     };
-    const int slot = slot_of_lane(lane);
+    // one lane of each quad writes the quad's two column maxima
+    const int qcol = tile_col(4 * ((lane >> 2) & 1) + 2 * ((lane >> 3) & 1) + ((lane >> 4) & 1), h);
+    auto write_cols = [&](int st, int tt, float c0, float c1) TWINKV_INLINE {
+      if ((lane & 3) == 0) {
+        colpart[st % 3][wave][tt * 32 + qcol] = c0;
+        colpart[st % 3][wave][tt * 32 + qcol + 16] = c1;
+      }
+    };
     auto flush_cols = [&](int st, int tt, bool live) TWINKV_INLINE {
-      float v = reduce_scatter16(colmax);
-      if (!live) v = -__builtin_inff();  // a masked tile is added after the sweep
-      if ((lane & 1) == 0) colpart[st % 3][wave][tt * 32 + tile_col(slot, h)] = v;
+      float c0, c1;
+      reduce_cols(colmax, c0, c1);
+      if (!live) c0 = c1 = -__builtin_inff();  // a masked tile is added after the sweep
+      write_cols(st, tt, c0, c1);
     };
     auto merge_stage = [&](int st) TWINKV_INLINE {
       for (int c = tid; c < SC; c += NT) {
@@ -445,7 +456,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
         const int c0 = tile * 32;
         if (c0 >= N) break;  // past the end (wave-uniform); these columns are never merged
         if (c0 + 31 <= rlo + w) {  // no pair of this tile has j - i > w for this wave
-          if ((lane & 1) == 0) colpart[st % 3][wave][tt * 32 + tile_col(slot, h)] = -__builtin_inff();
+          write_cols(st, tt, -__builtin_inff(), -__builtin_inff());
           continue;
         }
         const bool live = c0 > rhi + w && c0 + 31 < N;  // wave-uniform
