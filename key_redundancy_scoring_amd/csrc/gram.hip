@@ -133,20 +133,16 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
   // ---- byte offsets of this lane's stage loads and A-operand reads.  Load t
   // of a stage reads column (tid + NT*t)/CH at a swizzled chunk, and the
   // A operand of tile tt reads column 32*tt + lrow.  The swizzle repeats
-  // every 64 columns (d = 64) or 16 (d = 128), so the per-lane part of either
-  // address depends only on the parity of t or tt; the rest is a uniform
-  // stride (an SGPR base or an instruction offset).
-  static_assert((2 * NT / CH) % (CH == 8 ? 64 : 16) == 0 && 64 % (CH == 8 ? 64 : 16) == 0, "swizzle period");
-  uint32_t ld_off[2];
-  uint32_t a_off[2][KS];
+  // every 16 columns, so the per-lane part of either address is the same for
+  // every t and tt; the rest is a uniform stride (an SGPR base or an
+  // instruction offset).
+  static_assert((NT / CH) % kSwzPeriod == 0 && 32 % kSwzPeriod == 0, "swizzle period");
+  uint32_t ld_off, a_off[KS];
+  {
+    const int c = tid / CH;
+    ld_off = (uint32_t)((c * CH + ((tid % CH) ^ swz<CH>(c))) * 16);
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int q = tid + NT * p;
-    const int c = q / CH;
-    ld_off[p] = (uint32_t)((c * CH + ((q % CH) ^ swz<CH>(c))) * 16 - p * NT * 16);
-    const int cp = 32 * p + lrow;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) a_off[p][s] = (uint32_t)((cp * CH + ((2 * s + h) ^ swz<CH>(cp))) * 16 - p * 32 * CH * 16);
+    for (int s = 0; s < KS; ++s) a_off[s] = (uint32_t)((lrow * CH + ((2 * s + h) ^ swz<CH>(lrow))) * 16);
   }
 
   // ---- stage issue: direct loads into one LDS buffer.  A stage whose
@@ -157,7 +153,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
     if (col0 + SC <= ncols) {
       const char* base = reinterpret_cast<const char*>(Cg + (size_t)col0 * CH);
 #pragma unroll
-      for (int t = 0; t < LOADS; ++t) dma16(base + (size_t)NT * 16 * t + ld_off[t & 1], &sb.keys[NT * t + wave * 64]);
+      for (int t = 0; t < LOADS; ++t) dma16(base + (size_t)NT * 16 * t + ld_off, &sb.keys[NT * t + wave * 64]);
       if (wave < SC / 64) {
         dma4(crinv_g + col0 + tid, &sb.rinv[wave * 64]);
         dma4(cpos_g + col0 + tid, &sb.pos[wave * 64]);
@@ -170,7 +166,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
       // column tid/CH + (NT/CH)*t of the stage, chunk as in ld_off
       const int c = col0 + tid / CH + (NT / CH) * t;
       const int col = c < lastc ? c : lastc;
-      dma16(reinterpret_cast<const char*>(Cg + (size_t)col * CH) + (ld_off[t & 1] & (CH * 16 - 1)),
+      dma16(reinterpret_cast<const char*>(Cg + (size_t)col * CH) + (ld_off & (CH * 16 - 1)),
             &sb.keys[NT * t + wave * 64]);
     }
     if (wave < SC / 64) {
@@ -181,12 +177,11 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
   };
 
   // ---- per-tile pieces
-  // par = tt & 1
-  auto load_a = [&](const Stage<D, SC>& sb, int tt, int par, bf16x8 (&A)[KS]) TWINKV_INLINE {
+  auto load_a = [&](const Stage<D, SC>& sb, int tt, bf16x8 (&A)[KS]) TWINKV_INLINE {
     const char* kb = reinterpret_cast<const char*>(sb.keys) + tt * 32 * CH * 16;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + (par ? a_off[1][s] : a_off[0][s])));
+      A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + a_off[s]));
   };
   auto load_rv = [&](const Stage<D, SC>& sb, int tt, float (&rv)[16]) TWINKV_INLINE {
 #pragma unroll
@@ -271,7 +266,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
   __syncthreads();
   if (nstages > 1) issue(SC, buf1);
   if (nstages > 0) {
-    load_a(buf0, 0, 0, A);
+    load_a(buf0, 0, A);
 #pragma unroll
     for (int b = 0; b < RB; ++b) mfma_block(A, b, acc[b]);
     load_rv(buf0, 0, rv);
@@ -287,7 +282,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
 #pragma unroll 1
     for (int tt = 0; tt < TILES - 1; ++tt) {
       const int tile = st * TILES + tt;
-      load_a(cur, tt + 1, (tt + 1) & 1, A);
+      load_a(cur, tt + 1, A);
       const bool live = ((mbits >> tt) & 1u) == 0u;
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
@@ -304,7 +299,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void gram_kernel(GramArgs a)
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     if (st + 2 < nstages) issue((st + 2) * SC, cur);
-    if (more) load_a(nxt, 0, 0, A);
+    if (more) load_a(nxt, 0, A);
     const int tile = st * TILES + TILES - 1;
     const bool live = ((mbits >> (TILES - 1)) & 1u) == 0u;
 #pragma unroll

@@ -96,10 +96,12 @@ __device__ __forceinline__ int unpack_idx(uint64_t u, uint64_t idx_mask) { retur
 // Chunk k of column c lives at slot c*CH + (k ^ swz(c)).  For the A-operand
 // reads (lane l reads chunk k of column l mod 32) this puts any 8 consecutive
 // lanes on distinct 16-byte bank groups of a 128-byte row and any 16 on
-// distinct groups of a 256-byte row.
+// distinct groups of a 256-byte row.  It repeats every kSwzPeriod columns, so
+// the per-lane part of an address is the same for every 32-column tile.
+constexpr int kSwzPeriod = 16;
 template <int CH>
 __device__ __forceinline__ int swz(int c) {
-  return CH == 8 ? ((c ^ (c >> 3)) & 7) : (c & 15);
+  return CH == 8 ? ((c ^ ((c >> 3) & 1)) & 7) : (c & 15);
 }
 
 // column offset (within a 32-column tile) of accumulator r in half-wave h

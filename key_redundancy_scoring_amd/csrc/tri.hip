@@ -235,18 +235,15 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
 
   // stage-load and A-operand offsets: load t of a stage reads column
   // (tid + NT*t)/CH at a swizzled chunk, the A operand of tile tt reads column
-  // 32*tt + lrow; both depend per lane only on the parity of t or tt
-  static_assert((2 * NT / CH) % (CH == 8 ? 64 : 16) == 0 && 64 % (CH == 8 ? 64 : 16) == 0, "swizzle period");
-  uint32_t ld_off[2];
-  uint32_t a_off[2][KS];
+  // 32*tt + lrow; the swizzle repeats within both strides, so the per-lane
+  // part of either address is the same for every t and tt
+  static_assert((NT / CH) % kSwzPeriod == 0 && 32 % kSwzPeriod == 0, "swizzle period");
+  uint32_t ld_off, a_off[KS];
+  {
+    const int c = tid / CH;
+    ld_off = (uint32_t)((c * CH + ((tid % CH) ^ swz<CH>(c))) * 16);
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int q = tid + NT * p;
-    const int c = q / CH;
-    ld_off[p] = (uint32_t)((c * CH + ((q % CH) ^ swz<CH>(c))) * 16 - p * NT * 16);
-    const int cp = 32 * p + lrow;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) a_off[p][s] = (uint32_t)((cp * CH + ((2 * s + h) ^ swz<CH>(cp))) * 16 - p * 32 * CH * 16);
+    for (int s = 0; s < KS; ++s) a_off[s] = (uint32_t)((lrow * CH + ((2 * s + h) ^ swz<CH>(lrow))) * 16);
   }
 
 #pragma unroll 1
@@ -288,7 +285,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
       if (col0 + SC <= ncols) {
         const char* base = reinterpret_cast<const char*>(Cg + (size_t)col0 * CH);
 #pragma unroll
-        for (int u = 0; u < LOADS; ++u) dma16(base + (size_t)NT * 16 * u + ld_off[u & 1], &sb.keys[NT * u + wave * 64]);
+        for (int u = 0; u < LOADS; ++u) dma16(base + (size_t)NT * 16 * u + ld_off, &sb.keys[NT * u + wave * 64]);
         if (wave < SC / 64) dma4(crinv + col0 + tid, &sb.rinv[wave * 64]);
         return;
       }
@@ -297,7 +294,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
       for (int u = 0; u < LOADS; ++u) {
         const int c = col0 + tid / CH + (NT / CH) * u;
         const int col = c < lastc ? c : lastc;
-        dma16(reinterpret_cast<const char*>(Cg + (size_t)col * CH) + (ld_off[u & 1] & (CH * 16 - 1)),
+        dma16(reinterpret_cast<const char*>(Cg + (size_t)col * CH) + (ld_off & (CH * 16 - 1)),
               &sb.keys[NT * u + wave * 64]);
       }
       if (wave < SC / 64) {
@@ -305,11 +302,11 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
         dma4(crinv + col, &sb.rinv[wave * 64]);
       }
     };
-    auto load_a = [&](const StageK<D, SC>& sb, int tt, int par, bf16x8 (&A)[KS]) TWINKV_INLINE {
+    auto load_a = [&](const StageK<D, SC>& sb, int tt, bf16x8 (&A)[KS]) TWINKV_INLINE {
       const char* kb = reinterpret_cast<const char*>(sb.keys) + tt * 32 * CH * 16;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + (par ? a_off[1][s] : a_off[0][s])));
+        A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + a_off[s]));
     };
     auto load_rv = [&](const StageK<D, SC>& sb, int tt, float (&rv)[16]) TWINKV_INLINE {
 #pragma unroll
@@ -460,7 +457,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
           continue;
         }
         const bool live = c0 > rhi + w && c0 + 31 < N;  // wave-uniform
-        load_a(cur, tt, tt & 1, A);
+        load_a(cur, tt, A);
         load_rv(cur, tt, rv);
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
@@ -479,7 +476,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
 #pragma unroll 1
       for (int tt = 0; tt < TILES - 1; ++tt) {
         const int tile = tile0 + st * TILES + tt;
-        load_a(cur, tt + 1, (tt + 1) & 1, A);
+        load_a(cur, tt + 1, A);
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
           epilogue(acc[b], b, rv, true, tile, tile * 32);
@@ -494,7 +491,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
       __syncthreads();
       if (st >= 1) merge_stage(st - 1);
       if (st + 2 < nstages) issue((st + 2) * SC, cur);
-      if (more) load_a(nxt, 0, 0, A);
+      if (more) load_a(nxt, 0, A);
       const int tile = tile0 + st * TILES + TILES - 1;
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
@@ -522,7 +519,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __syncthreads();
         if (nd + 1 < nstages) issue((nd + 1) * SC, buf1);
-        load_a(buf0, 0, 0, A);
+        load_a(buf0, 0, A);
 #pragma unroll
         for (int b = 0; b < RB; ++b) mfma_block(A, b, acc[b]);
         load_rv(buf0, 0, rv);
@@ -707,13 +704,9 @@ __global__ __launch_bounds__(256, S::D == 64 ? 2 : 1) void tri_colres_kernel(Tri
   if (tid == 0) qcount = 0;
   __syncthreads();
 
-  uint32_t a_off[2][KS];
+  uint32_t a_off[KS];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int cp = 32 * p + lrow;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) a_off[p][s] = (uint32_t)((cp * CH + ((2 * s + h) ^ swz<CH>(cp))) * 16 - p * 32 * CH * 16);
-  }
+  for (int s = 0; s < KS; ++s) a_off[s] = (uint32_t)((lrow * CH + ((2 * s + h) ^ swz<CH>(lrow))) * 16);
 
   // exact cosine of position k (chunks kc of this lane's half) with staged row
   // c; both lanes of the position call it together
@@ -731,7 +724,7 @@ __global__ __launch_bounds__(256, S::D == 64 ? 2 : 1) void tri_colres_kernel(Tri
     const char* kb = reinterpret_cast<const char*>(blk.keys) + tt * 32 * CH * 16;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + ((tt & 1) ? a_off[1][s] : a_off[0][s])));
+      A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + a_off[s]));
     f32x16 acc = (f32x16){};
 #pragma unroll
     for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], bk[s], acc, 0, 0, 0);
