@@ -66,8 +66,11 @@ PEAK_FP64_TFLOPS = 78.6
 # the oracle's whole step costs O(N^2 d) fp64 work per head (15-20 s of one
 # host core at N = 32768); longer heads get no CPU baseline
 CPU_BASELINE_MAX_N = 32768
-SOURCES = {"score": os.path.join(ROOT, "key_redundancy_scoring_amd", "csrc", "tri.hip"),
-           "repair": os.path.join(ROOT, "key_redundancy_scoring_amd", "csrc", "gram.hip")}
+_CSRC = os.path.join(ROOT, "key_redundancy_scoring_amd", "csrc")
+# the sources of each mode's dominant kernel (its HBM counters are kept only
+# while these are unchanged)
+SOURCES = {"score": [os.path.join(_CSRC, "tri.hip"), os.path.join(_CSRC, "sweep.h")],
+           "repair": [os.path.join(_CSRC, "gram.hip"), os.path.join(_CSRC, "sweep.h")]}
 # the dominant kernel of each mode per head dim, as the kernel trace names it
 SCORE_KERNEL = {64: "tri_sweep_kernel<GramShape<64, 3, 4, 256, 2>>",
                 128: "tri_sweep_kernel<GramShape<128, 2, 4, 128, 2>>"}
@@ -76,24 +79,28 @@ REPAIR_KERNEL = {64: "gram_kernel<GramShape<64, 2, 4, 128, 3>>",
 
 # HBM traffic of one launch of the dominant kernel, from rocprofv3 FETCH_SIZE /
 # WRITE_SIZE (KiB per dispatch) scaled by the counters' reading for a plain
-# device copy of known size; keyed by the sha256 of the kernel's source file
-# at the time the counters were taken, so a changed kernel reports null.
+# device copy of known size; keyed by the sha256 of the kernel's sources
+# (source_hash) at the time the counters were taken, so a changed kernel
+# reports null.
 MEASURED_TRAFFIC: dict = {
-    "45624f51ecd5c02e9d2eeb4f8fc2fb96624c598fbb65e95ccfde8a17eac1e0c5": {
+    "daf5c0bc42f60151be3a04592499ab89f7c90f742b478f81ac718d0cfc063443": {
         "workload": (128, 32768, 64),
         "kernel": "tri_sweep_kernel<GramShape<64, 3, 4, 256, 2>>",
-        # FETCH_SIZE 2566311.3 KiB x 1.99994 (a 1 GiB copy reads 524302.6 KiB),
-        # WRITE_SIZE 1527334.3 KiB x 1.0 (the same copy writes 1048576 KiB)
-        "fetch_bytes": 5255657458,
-        "write_bytes": 1563990368,
-        "bytes_per_launch": 6819647826,
+        # FETCH_SIZE 2283057.3 KiB x 1.99994 (a 1 GiB copy reads 524302.5 KiB),
+        # WRITE_SIZE 1460898.5 KiB x 1.0 (the same copy writes 1048576 KiB)
+        "fetch_bytes": 4675572177,
+        "write_bytes": 1495960032,
+        "bytes_per_launch": 6171532209,
     },
 }
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def algorithmic_gram_flops(N: int, d: int, window: int, G: int) -> float:
