@@ -75,7 +75,7 @@ SOURCES = {"score": [os.path.join(_CSRC, "tri.hip"), os.path.join(_CSRC, "sweep.
 SCORE_KERNEL = {64: "tri_sweep_kernel<GramShape<64, 3, 4, 256, 2>>",
                 128: "tri_sweep_kernel<GramShape<128, 2, 4, 128, 2>>"}
 REPAIR_KERNEL = {64: "gram_kernel<GramShape<64, 2, 4, 128, 3>>",
-                 128: "gram_kernel<GramShape<128, 2, 4, 128, 2>>"}
+                 128: "gram_kernel<GramShape<128, 3, 4, 128, 2>>"}
 
 # HBM traffic of one launch of the dominant kernel, from rocprofv3 FETCH_SIZE /
 # WRITE_SIZE (KiB per dispatch) scaled by the counters' reading for a plain
