@@ -14,10 +14,11 @@
 //     per half-row;
 //   * the column side (j's maximum over the block's rows) is scaled to the
 //     cosine, merged over the wave's row blocks in each lane, then over the
-//     32 lanes that share a column set by a reduce-scatter of v_permlane16_swap
-//     and DPP row mirrors, then over the workgroup's waves in LDS, and stored
-//     per (row block, column); its counts are added atomically (rare: only
-//     when some element of a block crosses tau).
+//     32 lanes that share a column set (a v_permlane16_swap step, then DPP
+//     row mirrors whose bank masks write each column only into the lanes
+//     that keep it, then quad reductions), then over the workgroup's waves in
+//     LDS, and stored per (row block, column); its counts are added
+//     atomically (rare: only when some element of a block crosses tau).
 // The resolve kernels then take, for every position, the largest of its row
 // side and of the column maxima of the row blocks before it, mark the
 // blocks whose maximum is within a margin of it, and re-sweep each such
@@ -25,11 +26,11 @@
 // row side's own best is made exact at the end of the sweep (the fused
 // fixup) over the first tile attaining each half-row's maximum; a row where
 // another tile comes within twice the fp32 error of that maximum is queued
-// for the exact resolve of resolve.hip instead.  Both sides merge through a 64-bit atomic maximum of (exact
-// cosine, position) in which the low 30 bits of the order-preserving image
-// of the cosine carry the position, so equal cosines go to the lowest
-// position.  A workgroup sweeps two row blocks, rb and nb-1-rb, so every
-// workgroup covers about the same number of columns.
+// for the exact resolve of resolve.hip instead.  Both sides merge through a
+// 64-bit atomic maximum of (exact cosine, position) in which the low bits of
+// the order-preserving image of the cosine carry the position, so equal
+// cosines go to the lowest position.  A workgroup sweeps two row blocks, rb
+// and nb-1-rb, so every workgroup covers about the same number of columns.
 #include <limits.h>
 
 #include "sweep.h"
