@@ -14,11 +14,12 @@
 //     per half-row;
 //   * the column side (j's maximum over the block's rows) is scaled to the
 //     cosine, merged over the wave's row blocks in each lane, then over the
-//     32 lanes that share a column set (a v_permlane16_swap step, then DPP
-//     row mirrors whose bank masks write each column only into the lanes
-//     that keep it, then quad reductions), then over the workgroup's waves in
-//     LDS, and stored per (row block, column); its counts are added
-//     atomically (rare: only when some element of a block crosses tau).
+//     32 lanes that share a column set (DPP row mirrors whose bank masks
+//     write each column only into the lanes that keep it, a
+//     v_permlane16_swap step across rows, then quad reductions), then over
+//     the workgroup's waves in LDS, and stored per (row block, column); its
+//     counts are added atomically (rare: only when some element of a block
+//     crosses tau).
 // The resolve kernels then take, for every position, the largest of its row
 // side and of the column maxima of the row blocks before it, mark the
 // blocks whose maximum is within a margin of it, and re-sweep each such
@@ -55,52 +56,66 @@ constexpr float kTieMargin = 2e-5f;
 
 // Column maxima of a tile over the 32 lanes of each half-wave.  The 16
 // accumulator values of a lane are 16 columns (tile_col(r, h)) of the lane's
-// row; the 32 lanes of a half-wave share those columns.  A swap across the
-// 16-lane rows pairs lanes l and l^16; inside a row, lane p pairs with 15 - p
-// and then with 7 - p (DPP mirrors): of each pair of values the lanes keep
-// one column, and the DPP bank mask (a bank is a group of four lanes of a
-// row) writes each column only into the lanes that keep it, so no lane
-// selects are needed; the last two pairings, inside 4-lane quads, reduce
-// fully.  On return every lane holds the maxima of column slots s and s + 8,
-// s = 4*b2 + 2*b3 + b4 (bk: bit k of the lane id).  The DPP reads follow
-// their inputs' writes by the two wait states the hardware requires.
+// row; the 32 lanes of a half-wave share those columns.  Inside a 16-lane
+// row, lane p pairs with 15 - p and then with 7 - p (DPP mirrors): of each
+// pair of values the lanes keep one column, and the DPP bank mask (a bank is
+// a group of four lanes of a row) writes each column only into the lanes
+// that keep it, so no lane selects are needed.  A swap across the rows then
+// pairs lanes l and l^16 on the four values left, and the last two pairings,
+// inside 4-lane quads, reduce fully.  On return every lane holds the maxima
+// of column slots s and s + 8, s = 4*b4 + 2*b2 + b3 (bk: bit k of the lane
+// id).  The DPP reads follow their inputs' writes by the two wait states the
+// hardware requires.
 __device__ __forceinline__ void reduce_cols(const float (&v)[16], float& c0, float& c1) {
-  float a[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    // odd rows of v[2k] swap with even rows of v[2k+1]: the even rows then
-    // hold slot 2k of lanes l and l^16, the odd rows slot 2k+1
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[2 * k]), __float_as_uint(v[2 * k + 1]), false, false);
-    a[k] = __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  }
+  float a0, a1, a2, a3, a4, a5, a6, a7;
+  // lanes 0-7 of a row keep the even slot of each pair, lanes 8-15 the odd
+  asm("s_nop 1\n\t"
+      "v_max_f32_dpp %0, %8, %8 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %0, %9, %9 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %1, %10, %10 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %1, %11, %11 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %2, %12, %12 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %2, %13, %13 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %3, %14, %14 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %3, %15, %15 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %4, %16, %16 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %4, %17, %17 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %5, %18, %18 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %5, %19, %19 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %6, %20, %20 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %6, %21, %21 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %7, %22, %22 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %7, %23, %23 row_mirror row_mask:0xf bank_mask:0xc"
+      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(a4), "=&v"(a5), "=&v"(a6), "=&v"(a7)
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(v[8]),
+        "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]));
   float b0, b1, b2, b3;
-  // lanes 0-7 of a row (banks 0, 1) keep a[2m], lanes 8-15 a[2m+1]
+  // lanes 0-3 and 8-11 (banks 0, 2) keep the even one of each pair
   asm("s_nop 1\n\t"
-      "v_max_f32_dpp %0, %4, %4 row_mirror row_mask:0xf bank_mask:0x3\n\t"
-      "v_max_f32_dpp %0, %5, %5 row_mirror row_mask:0xf bank_mask:0xc\n\t"
-      "v_max_f32_dpp %1, %6, %6 row_mirror row_mask:0xf bank_mask:0x3\n\t"
-      "v_max_f32_dpp %1, %7, %7 row_mirror row_mask:0xf bank_mask:0xc\n\t"
-      "v_max_f32_dpp %2, %8, %8 row_mirror row_mask:0xf bank_mask:0x3\n\t"
-      "v_max_f32_dpp %2, %9, %9 row_mirror row_mask:0xf bank_mask:0xc\n\t"
-      "v_max_f32_dpp %3, %10, %10 row_mirror row_mask:0xf bank_mask:0x3\n\t"
-      "v_max_f32_dpp %3, %11, %11 row_mirror row_mask:0xf bank_mask:0xc"
+      "v_max_f32_dpp %0, %4, %4 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_max_f32_dpp %0, %5, %5 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_max_f32_dpp %1, %6, %6 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_max_f32_dpp %1, %7, %7 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_max_f32_dpp %2, %8, %8 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_max_f32_dpp %2, %9, %9 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_max_f32_dpp %3, %10, %10 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_max_f32_dpp %3, %11, %11 row_half_mirror row_mask:0xf bank_mask:0xa"
       : "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3)
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
-  // lanes 0-3 and 8-11 (banks 0, 2) keep b[2m], lanes 4-7 and 12-15 b[2m+1];
-  // then each quad reduces both values
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(a4), "v"(a5), "v"(a6), "v"(a7));
+  // rows of 16 lanes: even rows keep b0 / b2, odd rows b1 / b3
+  auto r0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(b0), __float_as_uint(b1), false, false);
+  auto r1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(b2), __float_as_uint(b3), false, false);
+  float x0 = __builtin_fmaxf(__uint_as_float(r0[0]), __uint_as_float(r0[1]));
+  float x1 = __builtin_fmaxf(__uint_as_float(r1[0]), __uint_as_float(r1[1]));
   asm("s_nop 1\n\t"
-      "v_max_f32_dpp %0, %2, %2 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
-      "v_max_f32_dpp %0, %3, %3 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
-      "v_max_f32_dpp %1, %4, %4 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
-      "v_max_f32_dpp %1, %5, %5 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
-      "s_nop 1\n\t"
       "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
       "v_max_f32_dpp %1, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
       "s_nop 1\n\t"
       "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
       "v_max_f32_dpp %1, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
-      : "=&v"(c0), "=&v"(c1)
-      : "v"(b0), "v"(b1), "v"(b2), "v"(b3));
+      : "+v"(x0), "+v"(x1));
+  c0 = x0;
+  c1 = x1;
 }
 
 // fp32 <-> int with the same order (for atomic maxima of signed values)
@@ -366,7 +381,7 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
       }
     };
     // one lane of each quad writes the quad's two column maxima
-    const int qcol = tile_col(4 * ((lane >> 2) & 1) + 2 * ((lane >> 3) & 1) + ((lane >> 4) & 1), h);
+    const int qcol = tile_col(4 * ((lane >> 4) & 1) + 2 * ((lane >> 2) & 1) + ((lane >> 3) & 1), h);
     auto write_cols = [&](int st, int tt, float c0, float c1) TWINKV_INLINE {
       if ((lane & 3) == 0) {
         colpart[st % 3][wave][tt * 32 + qcol] = c0;
