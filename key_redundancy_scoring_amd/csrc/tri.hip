@@ -337,13 +337,14 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
     // first and last row position of the wave (rows past the end clamped)
     const int rlo = __builtin_amdgcn_readfirstlane(row0 < N ? row0 : (int)N - 1);
     const int rhi = __builtin_amdgcn_readfirstlane(row0 + RB * 32 - 1 < N ? row0 + RB * 32 - 1 : (int)N - 1);
-    // counts of y > tau*||k_i|| over the 16 values of block b (y > thr read
-    // off the sign of thr - y): the row's, and, one atomic per twin, each
-    // column's
-    auto count16 = [&](const f32x16& y, int b, int c0) TWINKV_INLINE {
+    // counts of y > tau*||k_i|| over the 16 values of block b: the row's,
+    // and, one atomic per twin, each column's.  Excluded entries hold -inf,
+    // and a zero key under a negative tau has thr = -inf, so the test is a
+    // compare (the sign of thr - y would be a NaN's there)
+    auto count16 = [&](const auto& y, int b, int c0) TWINKV_INLINE {
       uint32_t msk = 0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) msk |= (__float_as_uint(thr[b] - y[r]) >> 31) << r;
+      for (int r = 0; r < 16; ++r) msk |= (y[r] > thr[b] ? 1u : 0u) << r;
       cnt[b] += __popc(msk);
       while (msk != 0u) {
         const int r = __builtin_ctz(msk);
@@ -435,24 +436,25 @@ __global__ __launch_bounds__(64 * S::WAVES, S::OCC) void tri_sweep_kernel(TriArg
     // one tile's epilogue with every pair tested
     auto masked_epilogue = [&](f32x16& accb, int b, int tile, int c0) TWINKV_INLINE {
       const int i = row0 + 32 * b + lrow;
+      // entry r is column base + o, o = 8*(r>>2) + (r&3): a pair when o > lo
+      // (j - i > w) and o <= hi (j < N); a row past the end has none
+      const int base = c0 + 4 * h;
+      const int lo = i < N ? i + w - base : 64;
+      const int hi = (int)N - 1 - base;
       float yy[16];
-      int twins = 0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int col = c0 + tile_col(r, h);
-        const bool ok = i < N && col < N && col - i > w;
+        const int o = 8 * (r >> 2) + (r & 3);
+        const bool ok = o > lo && o <= hi;
         yy[r] = ok ? accb[r] * rv[r] : -__builtin_inff();
         const float z = ok ? yy[r] * rinvr[b] : -__builtin_inff();
         colmax[r] = (b == 0) ? z : __builtin_fmaxf(colmax[r], z);
-        const bool tw = ok && yy[r] > thr[b];
-        twins += tw ? 1 : 0;
-        if (tw) atomicAdd(&ccount_g[col], 1);
       }
-      cnt[b] += twins;
       const float m = max16(yy);
       second[b] = __builtin_amdgcn_fmed3f(m, best[b], second[b]);
       btile[b] = m > best[b] ? tile : btile[b];
       best[b] = __builtin_fmaxf(best[b], m);
+      if (__ballot(m > thr[b]) != 0ull) count16(yy, b, c0);  // excluded entries are -inf
     };
     // a stage run tile by tile; its data was issued before (into the buffer
     // of its parity)
